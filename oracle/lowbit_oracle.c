@@ -1,0 +1,237 @@
+/*
+ * lowbit_oracle.c -- plain, slow, obviously correct CPU oracle for
+ * weight-only low-bit RTN quantization, packing, dequantization and the fp64
+ * reference matrix product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path never
+ * calls it, and the two share no source, header, table or helper.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * (x86-64: float arithmetic is IEEE binary32 in SSE registers, so every
+ * float operation below is one correctly rounded IEEE operation).
+ *
+ * What the method computes, and where it comes from:
+ *  - "MinMax" quantization is plain round-to-nearest (RTN) with no calibration
+ *    data (BladeLLM model quantization, "Quantization algorithms", MinMax).
+ *  - The grid is the uniform asymmetric min-max grid of each row (OPTQ
+ *    reproducibility card, "Experiment Setup" row), or of each block of
+ *    consecutive input channels sharing one set of parameters (BladeLLM model
+ *    quantization, "block_wise_quant": S in R^{Ci/64 x Co}).
+ *  - For b bits, M = 2^b - 1:  scale = (max - min) / M,  zero = round(-min/scale),
+ *    q = clamp(round(w/scale) + zero, 0, M), with round-half-to-even.
+ *  - Codes are packed several to a machine word ("two 4bits ... into one 8bit",
+ *    "4x 2-bit weight in an uint8", "16 2-bits into an int32": [Feature
+ *    Request] 4bit and 2bit and 1bit quantization support, comments).
+ *  - At run time the low-bit weights are turned back into fp16 and multiplied
+ *    against fp16 activations (same feature request, elephantpanda's comment
+ *    on storing 4-bit weights and converting them with GPU cores).
+ *
+ * Readings taken where the pages leave a step open (each listed in the design
+ * notes of the repository):
+ *  R1 scale arithmetic: lo, hi are the fp16 weights widened to fp32 (exact);
+ *     d = hi - lo and s32 = d / M are single IEEE fp32 operations; the scale
+ *     is stored as s16 = fp16_rne(s32) and the STORED value is the scale used
+ *     for the zero point, the codes and the dequantization.
+ *  R2 a zero stored scale (hi == lo, or d/M below half the smallest fp16
+ *     subnormal) is replaced by 1.0.
+ *  R3 zero = (int32) rint(-lo / s) with the division in fp32; kept as a
+ *     signed, unclamped int32.
+ *  R4 q = clamp((int) rint(w / s) + zero, 0, M) with w / s one fp32 division.
+ *  R5 packing: per row, code k occupies bits [b*k, b*k + b) of a little-endian
+ *     bitstream of 32-bit words; 3-bit codes straddle word boundaries; every
+ *     row starts on a word boundary.
+ *  R6 dequantized weight: deq = fp16_rne((q - zero) * s), the product taken
+ *     exactly (in double it is exact: < 2^28 significant bits) and rounded
+ *     once to fp16.
+ *  R7 reference product: y[b][n] = sum_k x[b][k] * deq[n][k] in fp64.
+ */
+#include "lowbit_oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* IEEE 754 binary16 <-> binary64, written from the format's definition:  */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 is */
+/* the subnormal range (value = frac * 2^-24), exponent 31 is inf / NaN.  */
+/* ---------------------------------------------------------------------- */
+
+double orc_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value, ties to even (the default
+ * IEEE rounding-direction attribute).  The scaling by powers of two below is
+ * exact, and nearbyint() rounds to an integer in the current rounding mode,
+ * which is round-to-nearest-even by default. */
+uint16_t orc_f64_to_f16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7e00;
+    if (isinf(a)) return sign | 0x7c00;
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: the representable values are multiples of 2^-24 */
+        double m = nearbyint(ldexp(a, 24));
+        /* m == 1024 is the smallest normal number, whose encoding is 0x0400 */
+        return sign | (uint16_t)m;
+    }
+    int E;
+    frexp(a, &E);                 /* a = f * 2^E, f in [0.5, 1) */
+    int e = E - 1;                /* a = (2f) * 2^e, 2f in [1, 2) */
+    double m = nearbyint(ldexp(a, 10 - e));   /* 11-bit significand */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return sign | 0x7c00;         /* overflow rounds to infinity */
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+static int valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4; }
+
+/* group_size 0 means one group per row */
+static int64_t groups_of(int64_t K, int64_t group_size) {
+    return group_size == 0 ? 1 : K / group_size;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Quantization: group min/max, scale, zero point, codes (readings R1-R4). */
+/* The core accepts any group size that divides K; the shape rules of the  */
+/* GPU library are stricter and are enforced there, not here.              */
+/* ---------------------------------------------------------------------- */
+int orc_quantize_rtn(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
+                     uint8_t* codes, uint16_t* scales, int32_t* zeros) {
+    if (!w || !codes || !scales || !zeros || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return -1;
+    const int64_t g = group_size == 0 ? K : group_size;
+    const int64_t G = groups_of(K, group_size);
+    const int M = (1 << bits) - 1;
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < G; ++j) {
+            const uint16_t* wg = w + n * K + j * g;
+            /* step 1: the group's minimum and maximum (fp16 -> fp32 is exact) */
+            float lo = (float)orc_f16_to_f64(wg[0]);
+            float hi = lo;
+            for (int64_t k = 1; k < g; ++k) {
+                float v = (float)orc_f16_to_f64(wg[k]);
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            /* step 2: scale = (max - min) / M in fp32, stored as fp16 (R1, R2) */
+            float d = hi - lo;
+            float s32 = d / (float)M;
+            uint16_t s16 = orc_f64_to_f16((double)s32);
+            if ((s16 & 0x7fff) == 0) s16 = 0x3c00;
+            float s = (float)orc_f16_to_f64(s16);
+            /* step 3: zero point = round(-min / scale), half to even (R3) */
+            float zf = nearbyintf(-lo / s);
+            int32_t z = (int32_t)zf;
+            scales[n * G + j] = s16;
+            zeros[n * G + j] = z;
+            /* step 4: codes = clamp(round(w / scale) + zero, 0, M) (R4) */
+            for (int64_t k = 0; k < g; ++k) {
+                float v = (float)orc_f16_to_f64(wg[k]);
+                float t = nearbyintf(v / s);
+                int64_t q = (int64_t)t + (int64_t)z;
+                if (q < 0) q = 0;
+                if (q > M) q = M;
+                codes[n * K + j * g + k] = (uint8_t)q;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Packing (reading R5): code k of a row sits at bit b*k of the row's      */
+/* little-endian bitstream.                                                */
+/* ---------------------------------------------------------------------- */
+int orc_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed) {
+    if (!codes || !packed || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
+    if ((K * bits) % 32 != 0) return -1;
+    const int64_t words = K * bits / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        uint32_t* row = packed + n * words;
+        memset(row, 0, (size_t)words * sizeof(uint32_t));
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t q = codes[n * K + k];
+            int64_t bit = (int64_t)bits * k;
+            int64_t wi = bit / 32;
+            int off = (int)(bit % 32);
+            row[wi] |= q << off;
+            if (off + bits > 32) row[wi + 1] |= q >> (32 - off);
+        }
+    }
+    return 0;
+}
+
+int orc_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* codes) {
+    if (!codes || !packed || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
+    if ((K * bits) % 32 != 0) return -1;
+    const int64_t words = K * bits / 32;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint32_t* row = packed + n * words;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t bit = (int64_t)bits * k;
+            int64_t wi = bit / 32;
+            int off = (int)(bit % 32);
+            uint32_t q = row[wi] >> off;
+            if (off + bits > 32) q |= row[wi + 1] << (32 - off);
+            codes[n * K + k] = (uint8_t)(q & mask);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Dequantization (reading R6): deq = fp16_rne((q - zero) * scale).        */
+/* ---------------------------------------------------------------------- */
+int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,
+                int64_t N, int64_t K, int bits, int64_t group_size, uint16_t* deq) {
+    if (!codes || !scales || !zeros || !deq || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return -1;
+    const int64_t g = group_size == 0 ? K : group_size;
+    const int64_t G = groups_of(K, group_size);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t j = k / g;
+            double s = orc_f16_to_f64(scales[n * G + j]);
+            double qz = (double)((int64_t)codes[n * K + k] - (int64_t)zeros[n * G + j]);
+            deq[n * K + k] = orc_f64_to_f16(qz * s);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Reference product (reading R7): y = x * deq^T accumulated in fp64.      */
+/* ---------------------------------------------------------------------- */
+int orc_matmul_f64(const uint16_t* x, const uint16_t* deq, int64_t B, int64_t N, int64_t K,
+                   double* y) {
+    if (!x || !deq || !y || B < 0 || N < 0 || K <= 0) return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += orc_f16_to_f64(x[b * K + k]) * orc_f16_to_f64(deq[n * K + k]);
+            y[b * N + n] = acc;
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,44 @@
+/*
+ * lowbit_oracle.h -- declarations of the CPU oracle for weight-only low-bit
+ * round-to-nearest (RTN) quantization, bitstream packing, dequantization and
+ * the fp64 reference product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library and its Python binding) never calls it and shares no code with
+ * it.
+ *
+ * Conventions (all host pointers, dense row-major, caller-owned):
+ *   W      fp16 bit patterns  [N][K]   (N = output features, K = input features)
+ *   codes  uint8              [N][K]   values in [0, 2^bits - 1]
+ *   packed uint32             [N][K*bits/32]  per-row little-endian bitstream
+ *   scales fp16 bit patterns  [N][G]   G = K / group_size (group_size 0 = per-row)
+ *   zeros  int32              [N][G]
+ *   x      fp16 bit patterns  [B][K]
+ *   deq    fp16 bit patterns  [N][K]
+ *   y      double             [B][N]
+ * Every function returns 0 on success and -1 on a bad argument.
+ */
+#ifndef LOWBIT_ORACLE_H
+#define LOWBIT_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+double   orc_f16_to_f64(uint16_t h);
+uint16_t orc_f64_to_f16(double v);
+
+int orc_quantize_rtn(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
+                     uint8_t* codes, uint16_t* scales, int32_t* zeros);
+int orc_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed);
+int orc_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* codes);
+int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,
+                int64_t N, int64_t K, int bits, int64_t group_size, uint16_t* deq);
+int orc_matmul_f64(const uint16_t* x, const uint16_t* deq, int64_t B, int64_t N, int64_t K,
+                   double* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

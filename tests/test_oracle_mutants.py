@@ -1,0 +1,63 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each case copies ``oracle/lowbit_oracle.c`` to a temporary directory, applies
+one plausible mistake (a dropped term, a wrong sign or index, the wrong
+rounding rule, a transposed operand), compiles it with the oracle's own
+flags, and runs every pin against that broken build.  The mistake is planted
+in the oracle only, on the CPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import pins
+from oracle import Oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "lowbit_oracle.c")
+
+MUTANTS = {
+    "codes_round_half_away": ("float t = nearbyintf(v / s);", "float t = roundf(v / s);"),
+    "zero_round_half_away": ("float zf = nearbyintf(-lo / s);", "float zf = roundf(-lo / s);"),
+    "zero_wrong_sign": ("float zf = nearbyintf(-lo / s);", "float zf = nearbyintf(lo / s);"),
+    "scale_not_stored_as_fp16": ("float s = (float)orc_f16_to_f64(s16);",
+                                 "float s = (s32 == 0.0f) ? 1.0f : s32;"),
+    "levels_off_by_one": ("const int M = (1 << bits) - 1;", "const int M = (1 << bits);"),
+    "no_upper_clamp": ("if (q > M) q = M;", "if (q > M + 1) q = M;"),
+    "min_starts_at_zero": ("float lo = (float)orc_f16_to_f64(wg[0]);", "float lo = 0.0f;"),
+    "group_scan_drops_last": ("for (int64_t k = 1; k < g; ++k) {",
+                              "for (int64_t k = 1; k < g - 1; ++k) {"),
+    "pack_drops_straddle": ("if (off + bits > 32) row[wi + 1] |= q >> (32 - off);", ""),
+    "pack_msb_first": ("row[wi] |= q << off;", "row[wi] |= q << (32 - bits - off);"),
+    "dequant_adds_zero": ("(double)((int64_t)codes[n * K + k] - (int64_t)zeros[n * G + j])",
+                          "(double)((int64_t)codes[n * K + k] + (int64_t)zeros[n * G + j])"),
+    "dequant_wrong_group": ("int64_t j = k / g;", "int64_t j = k % G;"),
+    "f16_round_ties_away": ("double m = nearbyint(ldexp(a, 10 - e));",
+                            "double m = round(ldexp(a, 10 - e));"),
+    "f16_decode_wrong_bias": ("v = ldexp((double)(1024 + f), e - 25);",
+                              "v = ldexp((double)(1024 + f), e - 24);"),
+    "matmul_transposed": ("orc_f16_to_f64(deq[n * K + k])", "orc_f16_to_f64(deq[k * N + n])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "lowbit_oracle.c"
+    src.write_text(text.replace(old, new))
+    (tmp_path / "lowbit_oracle.h").write_text(
+        open(os.path.join(ROOT, "oracle", "lowbit_oracle.h")).read())
+    so = tmp_path / f"mutant_{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                    "-shared", "-o", str(so), str(src), "-lm"], check=True)
+    mutant = Oracle(str(so))
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
