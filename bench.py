@@ -1,0 +1,324 @@
+"""Benchmark: fused dequantize-GEMV of 3-bit per-row RTN weights at batch 1.
+
+Workload (the metric's): the two OPT-175B-shaped linear layers at 3 bits,
+per-row asymmetric min-max, word-straddling pack --- W 12288x12288 and fc1
+49152x12288 --- against one fp16 activation row.  A step is one batch-1
+forward through both layers: two lowbit_qgemv calls, each reading its layer's
+packed weights, fp16 scales and int32 zeros once from HBM.  The weights were
+quantized and packed on the GPU (lowbit_quantize_rtn) before the timed region
+and are resident in HBM; to keep the 256 MB last-level cache (MALL) from
+serving repeated reads, every step uses the next of several copies of the
+packed weights (>= 1 GB in total).
+
+value = algorithmic bytes of the step (packed words + scales + zeros + x + y)
+over the wall time of the timed steps; roofline.achieved = the same bytes per
+GEMV launch over the launches' average duration measured with HIP events on
+the launch stream.  The quantizer (lowbit_quantize_rtn) and the matrix-core
+product (lowbit_qgemm, Llama-70B MLP shape at batch 16/32/64) are measured in
+the same run as separate stages.  The CPU baseline times the C oracle's
+dequantize + fp64 product on a sample of rows of the same layers.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+                       [--no-stages] [--only-gemv]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix, published
+MALL_DEFEAT_BYTES = 1 << 30
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "qgemv_opt175b_3bit_traffic.json")
+GEMV_SOURCES = ["gemv.hip", "unit_decode.h", "common.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "weight_only_bit_rtn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def product_bytes(N: int, K: int, bits: int, group_size: int, B: int) -> int:
+    G = 1 if group_size == 0 else K // group_size
+    return N * K * bits // 8 + N * G * 2 + N * G * 4 + B * K * 2 + B * N * 2
+
+
+def quantize_bytes(N: int, K: int, bits: int, group_size: int) -> int:
+    G = 1 if group_size == 0 else K // group_size
+    return N * K * 2 + N * K * bits // 8 + N * G * 6
+
+
+class Prepared:
+    """A layer quantized on the GPU, with `copies` copies of its packed form."""
+
+    def __init__(self, lw, torch, layer, copies: int):
+        import numpy as np
+        self.layer = layer
+        dev = torch.device("cuda:0")
+        w = torch.from_numpy(layer.weights()).to(dev)
+        q = lw.quantize_rtn(w, layer.bits, layer.group_size, codes=False, packed=True)
+        self.w = w
+        self.copies = [(q["packed"], q["scales"], q["zeros"])]
+        for _ in range(copies - 1):
+            self.copies.append(tuple(t.clone() for t in self.copies[0]))
+        self.x = {B: torch.from_numpy(layer.activations(B)).to(dev) for B in layer.batches}
+        self.y = {B: torch.empty((B, layer.N), dtype=torch.float16, device=dev)
+                  for B in layer.batches}
+        self.np = np
+
+    def footprint(self) -> int:
+        L = self.layer
+        return product_bytes(L.N, L.K, L.bits, L.group_size, 0)
+
+
+def copies_for(footprint: int) -> int:
+    return max(2, math.ceil(MALL_DEFEAT_BYTES / max(footprint, 1)))
+
+
+def run_product(lw, prep: Prepared, B: int, c: int, stream: int, kernel: str) -> None:
+    L = prep.layer
+    packed, scales, zeros = prep.copies[c % len(prep.copies)]
+    raw = lw.qgemv_raw if kernel == "qgemv" else lw.qgemm_raw
+    st = raw(prep.x[B].data_ptr(), B, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+             L.N, L.K, L.bits, L.group_size, prep.y[B].data_ptr(), stream)
+    if st != 0:
+        raise RuntimeError(f"{kernel} failed: {lw.status_string(st)}")
+
+
+def time_launches(torch, fn, count: int):
+    """Average device time of `count` launches of fn(i), each bracketed by events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(count)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def measure_stages(lw, torch, stream: int, reps: int) -> dict:
+    import synth
+    stages = {}
+    # quantize + pack of the OPT-175B 3-bit layers (reads 2 B per weight)
+    for layer in synth.WORKLOADS["opt175b_3bit"]:
+        dev = torch.device("cuda:0")
+        w = torch.from_numpy(layer.weights()).to(dev)
+        G = 1
+        packed = torch.empty((layer.N, layer.K * layer.bits // 32), dtype=torch.int32, device=dev)
+        scales = torch.empty((layer.N, G), dtype=torch.float16, device=dev)
+        zeros = torch.empty((layer.N, G), dtype=torch.int32, device=dev)
+
+        def q(_):
+            st = lw.quantize_rtn_raw(w.data_ptr(), layer.N, layer.K, layer.bits, layer.group_size,
+                                     None, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                     stream)
+            if st != 0:
+                raise RuntimeError(lw.status_string(st))
+
+        q(0)
+        avg, med = time_launches(torch, q, reps)
+        nbytes = quantize_bytes(layer.N, layer.K, layer.bits, layer.group_size)
+        stages[f"quantize_pack/{layer.name}"] = {
+            "us": round(avg * 1e3, 2), "bytes": nbytes,
+            "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
+        del w, packed, scales, zeros
+    # every workload's products
+    for name, layers in synth.WORKLOADS.items():
+        for layer in layers:
+            prep = None
+            for B in layer.batches:
+                kern = "qgemv" if B <= lw.QGEMV_MAX_B else "qgemm"
+                if prep is None:
+                    fp = product_bytes(layer.N, layer.K, layer.bits, layer.group_size, 0)
+                    prep = Prepared(lw, torch, layer, copies_for(fp))
+                for i in range(3):
+                    run_product(lw, prep, B, i, stream, kern)
+                avg, med = time_launches(
+                    torch, lambda i: run_product(lw, prep, B, i, stream, kern), reps)
+                nbytes = product_bytes(layer.N, layer.K, layer.bits, layer.group_size, B)
+                gbps = nbytes / (avg * 1e-3) / 1e9
+                rec = {"kernel": kern, "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2),
+                       "bytes": nbytes, "GBps": round(gbps, 1),
+                       "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+                if kern == "qgemm":
+                    tflops = 2.0 * B * layer.N * layer.K / (avg * 1e-3) / 1e12
+                    rec["TFLOPs"] = round(tflops, 1)
+                    rec["mfma_frac"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
+                stages[f"{kern}/{layer.name}/B{B}"] = rec
+            del prep
+            torch.cuda.empty_cache()
+    return stages
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """The C oracle (single-threaded) on a bounded sample of the same layers."""
+    import numpy as np
+
+    import oracle
+    import synth
+    layers = synth.WORKLOADS["opt175b_3bit"]
+    rows_per_chunk = 256
+    nbytes = 0
+    rows_done = 0
+    t_total = 0.0
+    li = 0
+    while t_total < budget_s:
+        layer = layers[li % len(layers)]
+        li += 1
+        w = synth.normal_f16(rows_per_chunk, layer.K, layer.w_std, layer.seed + 1000 + li,
+                             synth.STREAM_W)
+        codes, scales, zeros = oracle.quantize_rtn(w, layer.bits, layer.group_size)
+        packed = oracle.pack(codes, layer.bits)
+        x = layer.activations(1)
+        t0 = time.perf_counter()
+        oracle.reference_y(x, packed, scales, zeros, layer.K, layer.bits, layer.group_size)
+        t_total += time.perf_counter() - t0
+        nbytes += product_bytes(rows_per_chunk, layer.K, layer.bits, layer.group_size, 1)
+        rows_done += rows_per_chunk
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{rows_done} weight rows ({rows_per_chunk}-row chunks alternating the "
+                      f"12288x12288 and 49152x12288 layers' shape, K=12288, 3-bit per-row) through "
+                      f"the oracle's unpack + exact fp16 dequant + fp64 product, batch 1; "
+                      f"{t_total:.1f} s single-threaded"}
+
+
+def load_traffic(avg_bytes_per_launch: int):
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemv_source_hash") != gemv_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=20)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the quantized GEMV path has no multi-GPU "
+              "component in this build (see the sharding notes in DESIGN.md); rerun with "
+              "--gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import weight_only_bit_rtn_amd as lw
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lw.load_library()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    layers = synth.WORKLOADS["opt175b_3bit"]
+    footprint = sum(product_bytes(L.N, L.K, L.bits, L.group_size, 0) for L in layers)
+    copies = copies_for(footprint)
+    log(f"[bench] preparing {len(layers)} layers, {copies} weight copies "
+        f"({copies * footprint / 1e9:.2f} GB)")
+    preps = [Prepared(lw, torch, L, copies) for L in layers]
+    for p in preps:
+        del p.w
+    torch.cuda.synchronize()
+    step_bytes = sum(product_bytes(L.N, L.K, L.bits, L.group_size, 1) for L in layers)
+
+    def step(i: int) -> None:
+        for p in preps:
+            run_product(lw, p, 1, i, stream, "qgemv")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes * args.steps / wall / 1e9
+
+    # per-launch device time of the same launches (HIP events on the launch stream)
+    per_layer = {}
+    total_ms = 0.0
+    for j, p in enumerate(preps):
+        avg, med = time_launches(torch, lambda i, p=p: run_product(lw, p, 1, i, stream, "qgemv"),
+                                 args.steps)
+        per_layer[p.layer.name] = (avg, med)
+        total_ms += avg
+    launches = len(preps)
+    avg_launch_ms = total_ms / launches
+    avg_bytes = step_bytes / launches
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
+    traffic = load_traffic(avg_bytes)
+
+    result = {
+        "metric": "packed-weight GB/s & % HBM peak, 3/4-bit dequant-GEMV batch 1 (us/layer)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "opt175b_3bit_gemv_b1",
+                   "layers": [f"{L.N}x{L.K}" for L in layers], "bits": 3,
+                   "group_size": "per-row", "batch": 1, "weight_copies": copies,
+                   "w_dist": "N(0,0.02) fp16", "x_dist": "N(0,1) fp16", "seed": 0},
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "us_per_layer": {name: round(avg * 1e3, 2) for name, (avg, med) in per_layer.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "qgemv_kernel<3,1,R,perrow>",
+                     "bytes_per_launch": int(avg_bytes),
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 3)},
+    }
+    if not args.no_stages:
+        log("[bench] stages")
+        result["stages"] = measure_stages(lw, torch, stream, args.stage_reps)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

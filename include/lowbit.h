@@ -1,0 +1,134 @@
+/*
+ * lowbit.h -- C ABI of liblowbit, weight-only low-bit round-to-nearest (RTN)
+ * quantized linear layers for AMD MI355X (gfx950).
+ *
+ * The method (sources are the pages this library was written from):
+ *  - Weights are quantized with "MinMax", i.e. round-to-nearest with no
+ *    calibration data (BladeLLM model quantization, "Quantization
+ *    algorithms", MinMax), on a uniform asymmetric min-max grid per output
+ *    row (OPTQ reproducibility card, "Experiment Setup" row) or per block of
+ *    consecutive input channels (BladeLLM model quantization,
+ *    "block_wise_quant": S in R^{Ci/group x Co}).
+ *  - For b bits, M = 2^b - 1, per group:  scale = (max - min) / M,
+ *    zero = round(-min / scale), q = clamp(round(w / scale) + zero, 0, M),
+ *    rounding half to even.
+ *  - Several codes share one machine word ([Feature Request] 4bit and 2bit
+ *    and 1bit quantization support: two 4-bit codes per byte, four 2-bit
+ *    codes per uint8, sixteen 2-bit codes per int32).
+ *  - The low-bit weights stay in GPU memory and are turned back into fp16 by
+ *    the GPU's own cores inside the matrix product (same feature request;
+ *    "weight_only_quant" in BladeLLM model quantization, "Quantization modes",
+ *    is the mode that pays off when memory bandwidth is the constraint).
+ *
+ * Exact arithmetic contract (identical in every entry point):
+ *  - lo, hi = min, max of the group's fp16 weights (widened to fp32, exact);
+ *    s32 = fl32(fl32(hi - lo) / M); the stored scale is s16 = fp16_rne(s32),
+ *    replaced by 1.0 when it is zero; s = (float)s16.
+ *  - zero = (int32) rint(fl32(-lo / s)), signed and not clamped.
+ *  - q = clamp((int) rint(fl32(w / s)) + zero, 0, M); divisions are IEEE
+ *    fp32 divisions, rint rounds half to even.
+ *  - Packing: per row, code k occupies bits [bits*k, bits*k + bits) of a
+ *    little-endian stream of 32-bit words; 3-bit codes straddle words; every
+ *    row starts on a word boundary.
+ *  - deq(q) = fp16_rne((q - zero) * s), the product exact before one
+ *    rounding;  y[b][n] = fp16_rne( sum_k x[b][k] * deq[n][k] ), accumulated
+ *    in fp32 (summation order unspecified).
+ *
+ * Layouts (dense, row-major, no strides; every pointer is a DEVICE pointer
+ * allocated and owned by the caller, 16-byte aligned):
+ *    w       fp16   [N][K]          N = output features, K = input features
+ *    codes   uint8  [N][K]
+ *    packed  uint32 [N][K*bits/32]
+ *    scales  fp16   [N][G]          G = K / group_size, or 1 when group_size == 0
+ *    zeros   int32  [N][G]
+ *    x       fp16   [B][K]
+ *    y       fp16   [B][N]
+ *  fp16 values are passed as their IEEE binary16 bit patterns.
+ *
+ * Shape rules (violations return LOWBIT_ERR_SHAPE):
+ *    K > 0, K % 32 == 0, (K * bits) % 128 == 0  (every packed row is whole
+ *    16-byte chunks); group_size == 0 or (group_size % 32 == 0 and
+ *    K % group_size == 0).  lowbit_quantize_rtn additionally needs
+ *    K <= LOWBIT_QUANTIZE_MAX_K.
+ *
+ * Errors: every entry point returns LOWBIT_OK (0) or a negative status.
+ * Arguments are validated on the host before anything is launched, so an
+ * error return means nothing was enqueued.  N == 0 (or B == 0) is a valid
+ * empty problem: nothing is launched and LOWBIT_OK is returned.  Kernels run
+ * asynchronously on hip_stream (a hipStream_t; NULL = the null stream); a
+ * device-side fault surfaces at the caller's next synchronization.  Inputs
+ * must be finite.  Outputs must not alias inputs.  The library allocates no
+ * memory and keeps no per-call state: calls on different streams may run
+ * concurrently as long as their output buffers do not overlap.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stdint.h>
+
+#ifndef LOWBIT_API
+#define LOWBIT_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_OK 0
+#define LOWBIT_ERR_ARG (-1)         /* null / misaligned pointer, negative size, B out of range */
+#define LOWBIT_ERR_SHAPE (-2)       /* K or group_size break the shape rules */
+#define LOWBIT_ERR_UNSUPPORTED (-3) /* bits not in {2, 3, 4} */
+#define LOWBIT_ERR_HIP (-4)         /* the HIP runtime refused a launch or query */
+
+#define LOWBIT_QUANTIZE_MAX_K 131072
+#define LOWBIT_QGEMV_MAX_B 15
+
+/*
+ * Quantize fp16 weights w[N][K] with min-max RTN (BladeLLM model
+ * quantization, "Quantization algorithms", MinMax; OPTQ reproducibility
+ * card, "Experiment Setup" row; groups along input channels per BladeLLM
+ * "block_wise_quant").  Writes scales[N][G] and zeros[N][G], plus the codes
+ * as bytes (codes_or_null) and/or packed words (packed_or_null); at least
+ * one of the two must be non-null.  The packed words equal those that
+ * lowbit_pack produces from the codes.
+ */
+LOWBIT_API int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int bits, int64_t group_size,
+                        uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                        int32_t* zeros, void* hip_stream);
+
+/*
+ * Pack byte codes[N][K] (each < 2^bits; higher bits are ignored) into
+ * packed[N][K*bits/32] (the feature request's several-codes-per-word
+ * storage; bit order as in the contract above).
+ */
+LOWBIT_API int lowbit_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
+                void* hip_stream);
+
+/*
+ * y[B][N] = x[B][K] * deq(packed)^T for 1 <= B <= LOWBIT_QGEMV_MAX_B: the
+ * fused dequantize-and-multiply of the feature request (weights kept
+ * low-bit in memory, turned into fp16 by the GPU at run time).  Bandwidth-
+ * bound: reads each packed word once.  B outside [0, 15] returns
+ * LOWBIT_ERR_ARG.
+ */
+LOWBIT_API int lowbit_qgemv(const void* x_f16, int64_t B, const uint32_t* packed, const uint16_t* scales_f16,
+                 const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
+                 void* y_f16, void* hip_stream);
+
+/*
+ * Same product for any B >= 0 through fp16 matrix-core (MFMA) tiles; meant
+ * for B >= 16, correct for every B.  Same arguments and contract as
+ * lowbit_qgemv.
+ */
+LOWBIT_API int lowbit_qgemm(const void* x_f16, int64_t B, const uint32_t* packed, const uint16_t* scales_f16,
+                 const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
+                 void* y_f16, void* hip_stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+LOWBIT_API const char* lowbit_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

@@ -5,16 +5,18 @@ packer or the matrix product lives here.  Both the CPU oracle's callers and
 the HIP path's callers draw their inputs from it, so the two sides see
 identical bytes.
 
-Generator: numpy's PCG64 bit generator seeded through ``SeedSequence([seed,
-stream])`` and its ``standard_normal(dtype=float32)`` sampler.  Each kind of
-input draws from its own stream so that changing one shape does not shift the
-others.  Samples are drawn in fp32, multiplied by the standard deviation in
-fp32, and rounded to fp16 (round-to-nearest-even, numpy's cast).  Large
-matrices are drawn in row chunks; the chunked draw is the same sequence as a
-single draw of the whole matrix.
+Generator: numpy's PCG64 bit generator and its ``standard_normal(dtype=
+float32)`` sampler.  A matrix is cut into blocks of ``ROWS_PER_BLOCK`` rows;
+block i of input kind ``stream`` draws from ``SeedSequence([seed, stream,
+i])``, so blocks can be drawn in parallel and a row's values do not depend on
+how many rows follow it.  Samples are drawn in fp32, multiplied by the
+standard deviation in fp32, and rounded to fp16 (round-to-nearest-even,
+numpy's cast).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -23,26 +25,38 @@ STREAM_W = 1        # weight matrix
 STREAM_X = 2        # activations
 STREAM_OUTLIER = 3  # choice of outlier input channels
 
-_CHUNK_ELEMS = 1 << 25
+ROWS_PER_BLOCK = 512
 
 
-def _rng(seed: int, stream: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream])))
+def _rng(seed: int, stream: int, block: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, block])))
+
+
+def _threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def normal_f16(rows: int, cols: int, std: float, seed: int, stream: int,
                col_scale: np.ndarray | None = None) -> np.ndarray:
     """fp16 matrix with entries fp16(fp32(N(0,1)) * std [* col_scale])."""
-    rng = _rng(seed, stream)
     out = np.empty((rows, cols), np.float16)
-    step = max(1, _CHUNK_ELEMS // max(cols, 1))
-    for r0 in range(0, rows, step):
-        r1 = min(rows, r0 + step)
-        a = rng.standard_normal(size=(r1 - r0, cols), dtype=np.float32)
+
+    def block(i: int) -> None:
+        r0 = i * ROWS_PER_BLOCK
+        r1 = min(rows, r0 + ROWS_PER_BLOCK)
+        a = _rng(seed, stream, i).standard_normal(size=(r1 - r0, cols), dtype=np.float32)
         a *= np.float32(std)
         if col_scale is not None:
             a *= col_scale[None, :]
         out[r0:r1] = a.astype(np.float16)
+
+    nblocks = (rows + ROWS_PER_BLOCK - 1) // ROWS_PER_BLOCK
+    if nblocks <= 1:
+        for i in range(nblocks):
+            block(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(block, range(nblocks)))
     return out
 
 

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export exactly the entry points ``include/lowbit.h``
+declares, and reject bad arguments on the host before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowbit.h")
+
+
+@pytest.fixture(scope="module")
+def lw():
+    import weight_only_bit_rtn_amd as lw
+    if not os.path.exists(lw.LIB_PATH):
+        from weight_only_bit_rtn_amd import build
+        build.build()
+    lw.load_library()
+    return lw
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LOWBIT_API\s+[\w\s\*]+?\b(lowbit_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_entry_points() == sorted(
+        ["lowbit_pack", "lowbit_qgemm", "lowbit_qgemv", "lowbit_quantize_rtn",
+         "lowbit_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lw):
+    lib = ctypes.CDLL(lw.LIB_PATH)
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+    assert set(lw.EXPORTED) == set(declared_entry_points())
+
+
+def test_header_constants_match_binding(lw):
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(LOWBIT_\w+)\s+\(?(-?\d+)\)?", text))
+    assert int(consts["LOWBIT_OK"]) == lw.LOWBIT_OK
+    assert int(consts["LOWBIT_ERR_ARG"]) == lw.LOWBIT_ERR_ARG
+    assert int(consts["LOWBIT_ERR_SHAPE"]) == lw.LOWBIT_ERR_SHAPE
+    assert int(consts["LOWBIT_ERR_UNSUPPORTED"]) == lw.LOWBIT_ERR_UNSUPPORTED
+    assert int(consts["LOWBIT_ERR_HIP"]) == lw.LOWBIT_ERR_HIP
+    assert int(consts["LOWBIT_QGEMV_MAX_B"]) == lw.QGEMV_MAX_B
+    assert int(consts["LOWBIT_QUANTIZE_MAX_K"]) == lw.QUANTIZE_MAX_K
+
+
+def test_status_strings(lw):
+    for st in (0, -1, -2, -3, -4, 17):
+        s = lw.status_string(st)
+        assert isinstance(s, str) and s
+    assert lw.status_string(0) == "ok"
+
+
+# Fake, never-dereferenced addresses: every call below must fail validation
+# (or be an empty problem) and return before any HIP call.
+P = 0x7F0000000000
+MIS = P + 4
+
+
+@pytest.mark.parametrize("call,status", [
+    # bit width
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 5, 0, P, P, P, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.pack_raw(P, 4, 128, 1, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.qgemv_raw(P, 1, P, P, P, 4, 128, 8, 0, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 0, 0, P, None), "UNSUPPORTED"),
+    # shapes
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 0, 4, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 48, 4, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 96, 3, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 96, 2, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 256, 4, 48, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 256, 4, 96, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 262144, 4, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.qgemv_raw(P, 1, P, P, P, 4, 160, 4, 64, P, None), "SHAPE"),
+    (lambda lw: lw.pack_raw(P, 4, 64, 3, P, None), "SHAPE"),
+    # arguments
+    (lambda lw: lw.quantize_rtn_raw(P, -1, 128, 4, 0, P, P, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 4, -32, P, P, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_raw(None, 4, 128, 4, 0, P, P, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 4, 0, None, None, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 4, 0, MIS, None, P, P, None), "ARG"),
+    (lambda lw: lw.pack_raw(None, 4, 128, 4, P, None), "ARG"),
+    (lambda lw: lw.qgemv_raw(P, 16, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemv_raw(P, -1, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemv_raw(P, 1, None, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 4, 0, MIS, None), "ARG"),
+    (lambda lw: lw.qgemm_raw(MIS, 1, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    # empty problems are valid and launch nothing
+    (lambda lw: lw.quantize_rtn_raw(None, 0, 128, 4, 0, None, None, None, None, None), "OK"),
+    (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),
+    (lambda lw: lw.qgemm_raw(None, 5, None, None, None, 0, 128, 4, 0, None, None), "OK"),
+    (lambda lw: lw.pack_raw(None, 0, 128, 4, None, None), "OK"),
+])
+def test_host_validation(lw, call, status):
+    want = {"OK": lw.LOWBIT_OK, "ARG": lw.LOWBIT_ERR_ARG, "SHAPE": lw.LOWBIT_ERR_SHAPE,
+            "UNSUPPORTED": lw.LOWBIT_ERR_UNSUPPORTED}[status]
+    assert call(lw) == want
+
+
+def test_binding_refuses_cpu_tensors(lw):
+    import torch
+    w = torch.zeros(4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        lw.quantize_rtn(w, 4, 0)

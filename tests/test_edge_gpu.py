@@ -1,0 +1,207 @@
+"""Edge cases of the HIP path against the oracle: ragged shapes that span
+several tiles with partial tails, every batch size of the matrix-vector
+kernel, batches around the matrix-core tile edges, degenerate groups (constant,
+all-zero, one-signed, tiny and far-from-zero weights that force the exact
+slow decode), round-half-to-even ties, empty problems and error returns."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import harness
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_bit_rtn_amd as lw
+    lw.load_library()
+    return lw
+
+
+def _to_gpu(a):
+    import torch
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _weights(kind: str, N: int, K: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    if kind == "wide":
+        return (rng.standard_normal((N, K)) * 30).astype(np.float16)
+    if kind == "tiny":           # scales far below 2^-7: exact slow decode
+        return (rng.standard_normal((N, K)) * 3e-5).astype(np.float16)
+    if kind == "offset":         # one-signed groups far from zero: large |zero|
+        return (100 + 0.1 * rng.standard_normal((N, K))).astype(np.float16)
+    if kind == "mixed":          # some rows tiny, some normal, some constant
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        w[::3] *= 1e-3
+        w[1::5] = 0.37
+        w[2::7] = 0.0
+        w[:, :: max(1, K // 7)] = -0.5
+        return w.astype(np.float16)
+    if kind == "positive":
+        return rng.uniform(0.1, 0.9, (N, K)).astype(np.float16)
+    if kind == "negative":
+        return rng.uniform(-2.0, -1.0, (N, K)).astype(np.float16)
+    if kind == "ties":           # the worked examples' values, tiled
+        base = np.array([-1.5, -0.5, 0.0, 0.5, 1.5, -0.5, 2.5, 0.25], np.float32)
+        return np.resize(base, (N, K)).astype(np.float16)
+    raise ValueError(kind)
+
+
+SHAPES = {
+    4: [(1, 32), (5, 96), (17, 2080), (67, 4128)],
+    2: [(1, 64), (5, 192), (17, 4160), (67, 8256)],
+    3: [(1, 128), (5, 384), (17, 4224), (67, 8320)],
+}
+
+
+def _groups(K):
+    gs = [0, 32]
+    for g in (96, 128, 192):
+        if K % g == 0:
+            gs.append(g)
+    return gs
+
+
+def _quant_cases():
+    for bits, shapes in SHAPES.items():
+        for (N, K) in shapes:
+            for g in _groups(K):
+                yield bits, N, K, g
+
+
+@pytest.mark.parametrize("bits,N,K,g", list(_quant_cases()))
+@pytest.mark.parametrize("kind", ["normal", "mixed"])
+def test_quantize_shapes(lw, bits, N, K, g, kind):
+    w = _weights(kind, N, K, seed=N * 131 + K + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    out = lw.quantize_rtn(_to_gpu(w), bits, g)
+    _sync()
+    assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16), scales.view(np.uint16))
+    assert np.array_equal(out["zeros"].cpu().numpy(), zeros)
+    assert np.array_equal(out["codes"].cpu().numpy(), codes)
+    assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), packed)
+
+
+@pytest.mark.parametrize("kind", ["wide", "tiny", "offset", "positive", "negative", "ties"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_degenerate(lw, kind, bits):
+    N, K = 9, 384 if bits != 2 else 448
+    if bits == 3:
+        K = 384
+    for g in (0, 32, 64 if K % 64 == 0 else 32):
+        w = _weights(kind, N, K, seed=bits)
+        codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+        for want_codes, want_packed in ((True, False), (False, True)):
+            out = lw.quantize_rtn(_to_gpu(w), bits, g, codes=want_codes, packed=want_packed)
+            _sync()
+            assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16),
+                                  scales.view(np.uint16)), (kind, g)
+            assert np.array_equal(out["zeros"].cpu().numpy(), zeros), (kind, g)
+            if want_codes:
+                assert np.array_equal(out["codes"].cpu().numpy(), codes), (kind, g)
+            if want_packed:
+                assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), packed), (kind, g)
+
+
+def _product_cases():
+    for bits, shapes in SHAPES.items():
+        for (N, K) in shapes:
+            for g in _groups(K)[:3]:
+                yield bits, N, K, g
+
+
+def _check_product(lw, w, bits, g, batches, kernel, stress=False):
+    import torch
+    N, K = w.shape
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    args = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, bits, g]
+    for B in batches:
+        x = harness.synth.normal_f16(B, K, 1.0, seed=B + 7, stream=2)
+        y = getattr(lw, kernel)(_to_gpu(x), *args)
+        torch.cuda.synchronize()
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g)
+        terms = harness.oracle_abs_y(x, packed, scales, zeros, K, bits, g) if stress else None
+        harness.assert_y_close(y.cpu().numpy(), y_ref,
+                               f"{kernel} bits={bits} N={N} K={K} g={g} B={B}", terms, K)
+
+
+@pytest.mark.parametrize("bits,N,K,g", list(_product_cases()))
+def test_qgemv_shapes(lw, bits, N, K, g):
+    w = _weights("normal", N, K, seed=N + 3 * K + bits)
+    _check_product(lw, w, bits, g, [1, 2, 3, 5, 8, 15] if K <= 4224 else [1, 4], "qgemv")
+
+
+@pytest.mark.parametrize("bits,N,K,g", list(_product_cases()))
+def test_qgemm_shapes(lw, bits, N, K, g):
+    w = _weights("normal", N, K, seed=N + 5 * K + bits)
+    _check_product(lw, w, bits, g, [1, 16, 17, 33, 64, 70], "qgemm")
+
+
+@pytest.mark.parametrize("kind", ["wide", "tiny", "offset", "mixed", "positive", "negative", "ties"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_products_degenerate(lw, kind, bits):
+    N, K = 70, 4224 if bits == 3 else 4160
+    w = _weights(kind, N, K, seed=11 * bits)
+    stress = kind in ("wide", "offset")
+    for g in (0, 64):
+        _check_product(lw, w, bits, g, [1, 4], "qgemv", stress)
+        _check_product(lw, w, bits, g, [16, 40], "qgemm", stress)
+
+
+def test_products_are_deterministic(lw):
+    import torch
+    N, K, bits, g = 1000, 4096, 4, 128
+    w = _weights("normal", N, K, 1)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    x = _to_gpu(harness.synth.normal_f16(8, K, 1.0, 0, 2))
+    a = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, bits, g]
+    for kern in ("qgemv", "qgemm"):
+        y1 = getattr(lw, kern)(x, *a)
+        y2 = getattr(lw, kern)(x, *a)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), kern
+
+
+def test_empty_problems_launch_nothing(lw):
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    dummy = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+    p = dummy.data_ptr()
+    assert lw.quantize_rtn_raw(p, 0, 128, 4, 0, p, p, p, p, stream) == lw.LOWBIT_OK
+    assert lw.pack_raw(p, 0, 128, 4, p, stream) == lw.LOWBIT_OK
+    assert lw.qgemv_raw(p, 0, p, p, p, 16, 128, 4, 0, p, stream) == lw.LOWBIT_OK
+    assert lw.qgemm_raw(p, 3, p, p, p, 0, 128, 4, 0, p, stream) == lw.LOWBIT_OK
+    torch.cuda.synchronize()
+    assert int(dummy.abs().sum()) == 0
+
+
+def test_error_returns_on_gpu(lw):
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    buf = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    p = buf.data_ptr()
+    assert lw.qgemv_raw(p, 16, p, p, p, 8, 128, 4, 0, p, stream) == lw.LOWBIT_ERR_ARG
+    assert lw.qgemv_raw(p, 1, p, p, p, 8, 128, 5, 0, p, stream) == lw.LOWBIT_ERR_UNSUPPORTED
+    assert lw.qgemm_raw(p, 1, p, p, p, 8, 96, 3, 0, p, stream) == lw.LOWBIT_ERR_SHAPE
+    assert lw.qgemm_raw(p + 2, 1, p, p, p, 8, 128, 4, 0, p, stream) == lw.LOWBIT_ERR_ARG
+    assert lw.quantize_rtn_raw(p, 8, 128, 4, 48, p, p, p, p, stream) == lw.LOWBIT_ERR_SHAPE
+    assert lw.quantize_rtn_raw(p, 8, 128, 4, 0, None, None, p, p, stream) == lw.LOWBIT_ERR_ARG
+    torch.cuda.synchronize()
+    assert int(buf.abs().sum()) == 0

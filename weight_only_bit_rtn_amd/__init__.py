@@ -1,0 +1,201 @@
+"""Python binding of liblowbit (weight-only 2/3/4-bit RTN linear layers, gfx950).
+
+Argument marshalling only: every step of quantization, packing and the
+dequantize-and-multiply products runs in the HIP kernels of ``liblowbit.so``,
+reached through its C ABI (``include/lowbit.h``).  torch is used for device
+memory and streams.  There is no CPU fallback: if the library is missing or
+no GPU is present the calls raise.
+
+Functions mirror the C entry points:
+
+  quantize_rtn(w, bits, group_size, codes=True, packed=True) -> dict
+  pack(codes, bits) -> packed
+  qgemv(x, packed, scales, zeros, K, bits, group_size) -> y      (1 <= B <= 15)
+  qgemm(x, packed, scales, zeros, K, bits, group_size) -> y      (any B)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblowbit.so")
+
+LOWBIT_OK = 0
+LOWBIT_ERR_ARG = -1
+LOWBIT_ERR_SHAPE = -2
+LOWBIT_ERR_UNSUPPORTED = -3
+LOWBIT_ERR_HIP = -4
+QGEMV_MAX_B = 15
+QUANTIZE_MAX_K = 131072
+
+EXPORTED = ("lowbit_quantize_rtn", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
+            "lowbit_status_string")
+
+_lib = None
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblowbit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m "
+                          f"weight_only_bit_rtn_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.lowbit_quantize_rtn.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp, vp, vp]
+    lib.lowbit_pack.argtypes = [vp, i64, i64, i32, vp, vp]
+    lib.lowbit_qgemv.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
+    lib.lowbit_qgemm.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
+    for name in ("lowbit_quantize_rtn", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.lowbit_status_string.argtypes = [ctypes.c_int]
+    lib.lowbit_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().lowbit_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != LOWBIT_OK:
+        raise LowbitError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _require_gpu_tensor(t, name: str, dtype) -> None:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def groups(K: int, group_size: int) -> int:
+    return 1 if group_size == 0 else K // group_size
+
+
+def packed_words(K: int, bits: int) -> int:
+    return K * bits // 32
+
+
+# ---------------------------------------------------------------------------
+# raw entry points (device pointers as ints; the caller owns every buffer)
+# ---------------------------------------------------------------------------
+def quantize_rtn_raw(w, N, K, bits, group_size, codes, packed, scales, zeros, stream) -> int:
+    return load_library().lowbit_quantize_rtn(w, N, K, bits, group_size, codes, packed, scales,
+                                              zeros, stream)
+
+
+def pack_raw(codes, N, K, bits, packed, stream) -> int:
+    return load_library().lowbit_pack(codes, N, K, bits, packed, stream)
+
+
+def qgemv_raw(x, B, packed, scales, zeros, N, K, bits, group_size, y, stream) -> int:
+    return load_library().lowbit_qgemv(x, B, packed, scales, zeros, N, K, bits, group_size, y,
+                                       stream)
+
+
+def qgemm_raw(x, B, packed, scales, zeros, N, K, bits, group_size, y, stream) -> int:
+    return load_library().lowbit_qgemm(x, B, packed, scales, zeros, N, K, bits, group_size, y,
+                                       stream)
+
+
+# ---------------------------------------------------------------------------
+# tensor front end
+# ---------------------------------------------------------------------------
+def quantize_rtn(w, bits: int, group_size: int, codes: bool = True, packed: bool = True,
+                 out: dict | None = None) -> dict:
+    """Min-max RTN quantization of fp16 ``w[N][K]`` on the GPU.
+
+    Returns a dict with ``scales`` (fp16 [N][G]), ``zeros`` (int32 [N][G]) and,
+    as requested, ``codes`` (uint8 [N][K]) and ``packed`` (int32 view of the
+    uint32 words, [N][K*bits/32]).  ``out`` may supply preallocated buffers.
+    """
+    torch = _torch()
+    _require_gpu_tensor(w, "w", torch.float16)
+    N, K = w.shape
+    G = groups(K, group_size)
+    out = dict(out or {})
+    dev = w.device
+    if "scales" not in out:
+        out["scales"] = torch.empty((N, G), dtype=torch.float16, device=dev)
+    if "zeros" not in out:
+        out["zeros"] = torch.empty((N, G), dtype=torch.int32, device=dev)
+    if codes and "codes" not in out:
+        out["codes"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if packed and "packed" not in out:
+        out["packed"] = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=dev)
+    st = quantize_rtn_raw(w.data_ptr(), N, K, bits, group_size,
+                          _ptr(out.get("codes") if codes else None),
+                          _ptr(out.get("packed") if packed else None),
+                          out["scales"].data_ptr(), out["zeros"].data_ptr(), _stream_handle(dev))
+    _check(st, "lowbit_quantize_rtn")
+    return out
+
+
+def pack(codes, bits: int, out=None):
+    torch = _torch()
+    _require_gpu_tensor(codes, "codes", torch.uint8)
+    N, K = codes.shape
+    if out is None:
+        out = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=codes.device)
+    _check(pack_raw(codes.data_ptr(), N, K, bits, out.data_ptr(), _stream_handle(codes.device)),
+           "lowbit_pack")
+    return out
+
+
+def _product(raw, name, x, packed, scales, zeros, K, bits, group_size, out):
+    torch = _torch()
+    _require_gpu_tensor(x, "x", torch.float16)
+    _require_gpu_tensor(packed, "packed", torch.int32)
+    _require_gpu_tensor(scales, "scales", torch.float16)
+    _require_gpu_tensor(zeros, "zeros", torch.int32)
+    B = x.shape[0]
+    N = packed.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x.shape[1] != K")
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float16, device=x.device)
+    _check(raw(x.data_ptr(), B, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), N, K,
+               bits, group_size, out.data_ptr(), _stream_handle(x.device)), name)
+    return out
+
+
+def qgemv(x, packed, scales, zeros, K: int, bits: int, group_size: int, out=None):
+    """y = x * deq(packed)^T, fp16 [B][N], 1 <= B <= 15 (VALU kernel)."""
+    return _product(qgemv_raw, "lowbit_qgemv", x, packed, scales, zeros, K, bits, group_size,
+                    out)
+
+
+def qgemm(x, packed, scales, zeros, K: int, bits: int, group_size: int, out=None):
+    """y = x * deq(packed)^T, fp16 [B][N], any B (matrix-core kernel)."""
+    return _product(qgemm_raw, "lowbit_qgemm", x, packed, scales, zeros, K, bits, group_size,
+                    out)

@@ -1,0 +1,148 @@
+// abi.hip -- the exported C entry points: argument checks, then launches.
+//
+// Every check runs on the host before anything is enqueued, so an error
+// return means the stream was left untouched.
+#include <stdint.h>
+
+#include <mutex>
+
+#include "../../include/lowbit.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace lowbit {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+}  // namespace lowbit
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_bits(int bits) {
+  return (bits == 2 || bits == 3 || bits == 4) ? LOWBIT_OK : LOWBIT_ERR_UNSUPPORTED;
+}
+
+int check_shape(int64_t N, int64_t K, int bits, int64_t group_size) {
+  if (N < 0 || K < 0 || group_size < 0) return LOWBIT_ERR_ARG;
+  if (N > INT32_MAX || K > INT32_MAX) return LOWBIT_ERR_SHAPE;
+  if (K == 0 || K % 32 != 0 || (K * bits) % 128 != 0) return LOWBIT_ERR_SHAPE;
+  if (group_size != 0 && (group_size % 32 != 0 || K % group_size != 0)) return LOWBIT_ERR_SHAPE;
+  return LOWBIT_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP; }
+
+int check_product(const void* x, int64_t B, const uint32_t* packed, const uint16_t* scales,
+                  const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
+                  const void* y) {
+  int rc = check_bits(bits);
+  if (rc != LOWBIT_OK) return rc;
+  if (B < 0) return LOWBIT_ERR_ARG;
+  rc = check_shape(N, K, bits, group_size);
+  if (rc != LOWBIT_OK) return rc;
+  if (N == 0 || B == 0) return LOWBIT_OK;
+  if (!x || !packed || !scales || !zeros || !y) return LOWBIT_ERR_ARG;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(zeros) ||
+      !aligned16(y))
+    return LOWBIT_ERR_ARG;
+  if ((int64_t)B * N > INT32_MAX || B > INT32_MAX) return LOWBIT_ERR_SHAPE;
+  return LOWBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int bits, int64_t group_size,
+                        uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                        int32_t* zeros, void* hip_stream) {
+  int rc = check_bits(bits);
+  if (rc != LOWBIT_OK) return rc;
+  rc = check_shape(N, K, bits, group_size);
+  if (rc != LOWBIT_OK) return rc;
+  if (K > LOWBIT_QUANTIZE_MAX_K) return LOWBIT_ERR_SHAPE;
+  if (N == 0) return LOWBIT_OK;
+  if (!w_f16 || !scales_f16 || !zeros || (!codes_or_null && !packed_or_null))
+    return LOWBIT_ERR_ARG;
+  if (!aligned16(w_f16) || !aligned16(scales_f16) || !aligned16(zeros) ||
+      (codes_or_null && !aligned16(codes_or_null)) ||
+      (packed_or_null && !aligned16(packed_or_null)))
+    return LOWBIT_ERR_ARG;
+  return hip_status(lowbit::launch_quantize(static_cast<const uint16_t*>(w_f16), N, K, bits,
+                                            group_size, codes_or_null, packed_or_null, scales_f16,
+                                            zeros, static_cast<hipStream_t>(hip_stream)));
+}
+
+int lowbit_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
+                void* hip_stream) {
+  int rc = check_bits(bits);
+  if (rc != LOWBIT_OK) return rc;
+  rc = check_shape(N, K, bits, 0);
+  if (rc != LOWBIT_OK) return rc;
+  if (N == 0) return LOWBIT_OK;
+  if (!codes || !packed || !aligned16(codes) || !aligned16(packed)) return LOWBIT_ERR_ARG;
+  return hip_status(
+      lowbit::launch_pack(codes, N, K, bits, packed, static_cast<hipStream_t>(hip_stream)));
+}
+
+int lowbit_qgemv(const void* x_f16, int64_t B, const uint32_t* packed, const uint16_t* scales_f16,
+                 const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
+                 void* y_f16, void* hip_stream) {
+  if (B > LOWBIT_QGEMV_MAX_B) return LOWBIT_ERR_ARG;
+  int rc = check_product(x_f16, B, packed, scales_f16, zeros, N, K, bits, group_size, y_f16);
+  if (rc != LOWBIT_OK || N == 0 || B == 0) return rc;
+  const uint16_t* x = static_cast<const uint16_t*>(x_f16);
+  uint16_t* y = static_cast<uint16_t*>(y_f16);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = lowbit::launch_qgemv(x, B, packed, scales_f16, zeros, N, K, bits, group_size, y, s);
+  if (e == hipErrorNotSupported)  // x too large for on-chip staging: matrix-core path
+    e = lowbit::launch_qgemm(x, B, packed, scales_f16, zeros, N, K, bits, group_size, y, s);
+  return hip_status(e);
+}
+
+int lowbit_qgemm(const void* x_f16, int64_t B, const uint32_t* packed, const uint16_t* scales_f16,
+                 const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
+                 void* y_f16, void* hip_stream) {
+  int rc = check_product(x_f16, B, packed, scales_f16, zeros, N, K, bits, group_size, y_f16);
+  if (rc != LOWBIT_OK || N == 0 || B == 0) return rc;
+  return hip_status(lowbit::launch_qgemm(static_cast<const uint16_t*>(x_f16), B, packed,
+                                         scales_f16, zeros, N, K, bits, group_size,
+                                         static_cast<uint16_t*>(y_f16),
+                                         static_cast<hipStream_t>(hip_stream)));
+}
+
+const char* lowbit_status_string(int status) {
+  switch (status) {
+    case LOWBIT_OK:
+      return "ok";
+    case LOWBIT_ERR_ARG:
+      return "invalid argument (null or misaligned pointer, negative size, batch out of range)";
+    case LOWBIT_ERR_SHAPE:
+      return "unsupported shape (K must be a positive multiple of 32 with K*bits a multiple of "
+             "128; group_size 0 or a multiple of 32 dividing K)";
+    case LOWBIT_ERR_UNSUPPORTED:
+      return "unsupported bit width (2, 3 or 4)";
+    case LOWBIT_ERR_HIP:
+      return "HIP runtime error while launching";
+    default:
+      return "unknown status";
+  }
+}
+
+}  // extern "C"

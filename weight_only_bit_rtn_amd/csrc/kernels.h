@@ -1,0 +1,28 @@
+// kernels.h -- internal host-side launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowbit {
+
+size_t quantize_lds_bytes(int64_t K, int64_t G);
+
+hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
+                           uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
+                           hipStream_t stream);
+
+hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
+                       hipStream_t stream);
+
+// VALU dequant-GEMV; returns hipErrorNotSupported when x does not fit the
+// on-chip staging budget (the caller then uses the MFMA path).
+hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
+                        const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream);
+
+hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
+                        const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream);
+
+}  // namespace lowbit
