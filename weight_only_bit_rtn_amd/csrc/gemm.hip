@@ -97,9 +97,10 @@ __global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(
     rowp_.z_lo = rowp_.z_hi = zrow[0];
     rowp_.v_lo = rowp_.v_hi = true;
 #pragma unroll
-    for (int c = 0; c < U::NCONST; ++c) rowfast &= make_consts<BITS>(rowp_, rowc[c]);
+    for (int c = 0; c < U::NCONST; ++c) rowfast &= make_consts<BITS, false>(rowp_, rowc[c]);
   }
 
+  const uint32_t mg = magic_register();
   f4_t acc[BT];
 #pragma unroll
   for (int bt = 0; bt < BT; ++bt) acc[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(
         } else {
           hp[c].v_lo = u.va;
           hp[c].v_hi = u.vb;
-          fast &= make_consts<BITS>(hp[c], cc[c]);
+          fast &= make_consts<BITS, false>(hp[c], cc[c]);
         }
       }
       if (full) fast = rowfast;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(
 #pragma unroll
       for (int c = 0; c < U::NCONST; ++c) {
         hp[c] = load_params<BITS>(srow, zrow, gsz, gshift, u, c);
-        fast &= make_consts<BITS>(hp[c], cc[c]);
+        fast &= make_consts<BITS, false>(hp[c], cc[c]);
       }
     }
 
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(
       for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          bop[s][e] = fast_pair<BITS>(w, 4 * s + e, cc[U::cset(4 * s + e)]);
+          bop[s][e] = fast_pair<BITS, false>(w, 4 * s + e, cc[U::cset(4 * s + e)], mg);
     } else {
 #pragma unroll
       for (int s = 0; s < S; ++s)

@@ -46,11 +46,14 @@ struct Unit<4> {
   __host__ __device__ static constexpr int pos(int s) { return (s & 1) ? 4 : 0; }
   __host__ __device__ static constexpr int cset(int) { return 0; }
   __host__ __device__ static constexpr bool uses(int p) { return p == 0 || p == 4; }
-  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s) {
+  static constexpr int NPOS = 2;  // distinct bit positions p, indexed by pidx
+  __host__ __device__ static constexpr int pidx(int p) { return p >> 2; }
+  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
+                                                    uint32_t mg) {
     const int d = s >> 2, i = s & 3;
     const uint32_t v = (i >= 2) ? (w[d] >> 8) : w[d];
     const uint32_t mask = (i & 1) ? 0x00F000F0u : 0x000F000Fu;
-    return (v & mask) | 0x64006400u;
+    return (v & mask) | mg;
   }
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[WORDS], int c) {
     return (w[c >> 3] >> (4 * (c & 7))) & 15u;
@@ -68,10 +71,13 @@ struct Unit<2> {
   }
   __host__ __device__ static constexpr int cset(int s) { return s >> 4; }
   __host__ __device__ static constexpr bool uses(int p) { return p <= 8 && (p & 1) == 0; }
-  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s) {
+  static constexpr int NPOS = 5;
+  __host__ __device__ static constexpr int pidx(int p) { return p >> 1; }
+  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
+                                                    uint32_t mg) {
     const int d = s >> 3, i = s & 7;
     const uint32_t v = (i < 5) ? w[d] : (w[d] >> 10);
-    return (v & (0x00030003u << pos(s))) | 0x64006400u;
+    return (v & (0x00030003u << pos(s))) | mg;
   }
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[WORDS], int c) {
     return (w[c >> 4] >> (2 * (c & 15))) & 3u;
@@ -98,6 +104,8 @@ struct Unit<3> {
   }
   __host__ __device__ static constexpr int cset(int) { return 0; }
   __host__ __device__ static constexpr bool uses(int p) { return p <= 7; }
+  static constexpr int NPOS = 8;
+  __host__ __device__ static constexpr int pidx(int p) { return p; }
   // Ten-code windows of one 32-code period (words d0 d1 d2 = stream bits
   // 0..95): window 0 = d0 (codes 0..9 at bits 0,3,..,27), window 1 = stream
   // bits 30..61 (codes 10..19), window 2 = stream bits 60..91 (codes 20..29).
@@ -106,7 +114,8 @@ struct Unit<3> {
            : m == 1 ? __builtin_amdgcn_alignbit(w[base + 1], w[base], 30)
                     : __builtin_amdgcn_alignbit(w[base + 2], w[base + 1], 28);
   }
-  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s) {
+  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
+                                                    uint32_t mg) {
     uint32_t v;
     if (s < 30) {
       const int m = s / 10, i = s % 10;
@@ -120,7 +129,7 @@ struct Unit<3> {
       // codes 30, 31 sit in bits 26..31 of d2: take byte 3 of each period
       v = __builtin_amdgcn_perm(w[5], w[2], 0x0c070c03u);
     }
-    return (v & (0x00070007u << pos(s))) | 0x64006400u;
+    return (v & (0x00070007u << pos(s))) | mg;
   }
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[WORDS], int c) {
     const int base = 3 * (c >> 5), bit = 3 * (c & 31), wi = bit >> 5, off = bit & 31;
@@ -151,63 +160,122 @@ struct HalfParams {
   bool v_lo, v_hi;
 };
 
+// Decode constants of one unit, indexed by bit position (pidx).
+//  hz[i] = 1024 + z * 2^p                          (both modes)
+//  hs[i] = s * 2^-p   (scaled mode: one accumulator per output)
+//  hs[0] = s          (per-position mode: the product comes out scaled by 2^p
+//                      and is accumulated separately per p, rescaled at the end)
 template <int BITS>
 struct Consts {
-  h2_t hz[Unit<BITS>::PMAX + 1];
-  h2_t hs[Unit<BITS>::PMAX + 1];
+  h2_t hz[Unit<BITS>::NPOS];
+  h2_t hs[Unit<BITS>::NPOS];
 };
 
-// Can the magic-number decode reproduce fp16_rne((q - z) * s) exactly?
-template <int PMAX>
-__device__ __forceinline__ bool half_fast(uint16_t sb, int32_t z) {
-  const int zp = z * (1 << PMAX);
-  const float s = h_bits_to_f32(sb);
-  const float sp = s * (1.0f / (float)(1 << PMAX));  // exact in fp32
-  const float back = (float)(_Float16)sp;
-  return zp >= -1024 && zp <= 1023 && back == sp;
+// Constants from integer operations on the bit patterns (so uniform inputs
+// stay in scalar registers):
+//  - 1024 + z*2^p for 0 <= z*2^p < 1024 is the fp16 pattern 0x6400 | (z << p);
+//  - s*2^-p is s with its exponent field lowered by p, exact as long as the
+//    result stays a normal number (exponent field of s above p).
+// Fast decode conditions per half (both modes): 0 <= z <= 1023 >> PMAX;
+//  scaled mode: exponent field of s >= PMAX + 1;
+//  per-position mode: s normal and s < 8, so that (q - z) * s * 2^p stays in
+//  fp16's normal range, where scaling by 2^p commutes with the rounding.
+template <int BITS, bool POS>
+__device__ __forceinline__ bool half_fast(uint32_t sb, int32_t z) {
+  constexpr int PMAX = Unit<BITS>::PMAX;
+  const bool zok = (uint32_t)z <= (1023u >> PMAX);
+  const bool sok = POS ? (sb >= 0x0400u && sb < 0x4800u) : (sb >= (uint32_t)(PMAX + 1) << 10);
+  return zok && sok;
 }
 
-template <int BITS>
+template <int BITS, bool POS>
 __device__ __forceinline__ bool make_consts(const HalfParams& hp, Consts<BITS>& c) {
   using U = Unit<BITS>;
-  constexpr int PMAX = U::PMAX;
-  const float sl = h_bits_to_f32(hp.s_lo), sh = h_bits_to_f32(hp.s_hi);
+  const uint32_t s2 = (uint32_t)hp.s_lo | ((uint32_t)hp.s_hi << 16);
+  const uint32_t z2 = ((uint32_t)hp.z_lo & 0xffffu) | ((uint32_t)hp.z_hi << 16);
+  const uint32_t keep = (hp.v_lo ? 0x0000ffffu : 0u) | (hp.v_hi ? 0xffff0000u : 0u);
 #pragma unroll
-  for (int p = 0; p <= PMAX; ++p) {
+  for (int p = 0; p <= U::PMAX; ++p) {
     if (!U::uses(p)) continue;
-    const float inv = 1.0f / (float)(1 << p);
-    const _Float16 hzl = (_Float16)(1024.0f + (float)(hp.z_lo * (1 << p)));
-    const _Float16 hzh = (_Float16)(1024.0f + (float)(hp.z_hi * (1 << p)));
-    const _Float16 hsl = hp.v_lo ? (_Float16)(sl * inv) : (_Float16)0.0f;
-    const _Float16 hsh = hp.v_hi ? (_Float16)(sh * inv) : (_Float16)0.0f;
-    c.hz[p] = h2_t{hzl, hzh};
-    c.hs[p] = h2_t{hsl, hsh};
+    const int i = U::pidx(p);
+    c.hz[i] = as_h2(0x64006400u + (z2 << p));
+    if (!POS) c.hs[i] = as_h2((s2 - ((uint32_t)p << 10) * 0x10001u) & keep);
   }
-  const bool fl = !hp.v_lo || half_fast<PMAX>(hp.s_lo, hp.z_lo);
-  const bool fh = !hp.v_hi || half_fast<PMAX>(hp.s_hi, hp.z_hi);
+  if (POS) c.hs[0] = as_h2(s2 & keep);
+  const bool fl = !hp.v_lo || half_fast<BITS, POS>(hp.s_lo, hp.z_lo);
+  const bool fh = !hp.v_hi || half_fast<BITS, POS>(hp.s_hi, hp.z_hi);
   return fl && fh;
 }
 
-// Exact dequantized pair of slot s the slow way: extract both codes, form the
-// exact product in fp64 and round it once to fp16.
+// Zero the scales of invalid halves (units past the end of the row).
+template <int BITS, bool POS>
+__device__ __forceinline__ void mask_consts(Consts<BITS>& c, bool v_lo, bool v_hi) {
+  using U = Unit<BITS>;
+  constexpr int n = POS ? 1 : U::NPOS;
+  const uint32_t keep = (v_lo ? 0x0000ffffu : 0u) | (v_hi ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int i = 0; i < n; ++i) c.hs[i] = as_h2(as_u32(c.hs[i]) & keep);
+}
+
+// fp16_rne((q - z) * s) for any code, zero point and scale: the product is
+// formed in fp32 and rounded to odd (its last bit records inexactness), which
+// makes the following fp32 -> fp16 rounding the correctly rounded result
+// (fp32 carries at least two more bits than fp16).
+__device__ __forceinline__ uint16_t exact_deq(int q, int z, float s) {
+  const float qz = (float)(q - z);  // exact: |q - z| < 2^24
+  const float p = qz * s;
+  const float e = __builtin_fmaf(qz, s, -p);  // exact remainder of the product
+  uint32_t pb = __builtin_bit_cast(uint32_t, p);
+  if (e != 0.0f && (pb & 1u) == 0u) pb += ((e > 0.0f) == (p > 0.0f)) ? 1u : 0xffffffffu;
+  return f32_to_h_bits(__builtin_bit_cast(float, pb));
+}
+
 template <int BITS>
 __device__ __forceinline__ h2_t slow_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
                                           const HalfParams& hp) {
   using U = Unit<BITS>;
   const int ql = (int)U::code(w, U::lo(s));
   const int qh = (int)U::code(w, U::hi(s));
-  const double sl = (double)h_bits_to_f32(hp.s_lo), sh = (double)h_bits_to_f32(hp.s_hi);
-  const uint16_t dl = hp.v_lo ? f64_to_h_bits((double)(ql - hp.z_lo) * sl) : (uint16_t)0;
-  const uint16_t dh = hp.v_hi ? f64_to_h_bits((double)(qh - hp.z_hi) * sh) : (uint16_t)0;
+  const uint16_t dl = hp.v_lo ? exact_deq(ql, hp.z_lo, h_bits_to_f32(hp.s_lo)) : (uint16_t)0;
+  const uint16_t dh = hp.v_hi ? exact_deq(qh, hp.z_hi, h_bits_to_f32(hp.s_hi)) : (uint16_t)0;
   return as_h2((uint32_t)dl | ((uint32_t)dh << 16));
 }
 
+// Code c of a unit whose words are stored column-wise in LDS (word i of lane
+// l at w[i * 64 + l]); c may be a run-time value.
 template <int BITS>
+__device__ __forceinline__ uint32_t unit_code_lds(const uint32_t* w, int lane, int c) {
+  int bit;
+  if constexpr (BITS == 3)
+    bit = 96 * (c >> 5) + 3 * (c & 31);
+  else
+    bit = BITS * c;
+  const int wi = bit >> 5, off = bit & 31;
+  uint32_t v = w[wi * 64 + lane] >> off;
+  if (off + BITS > 32) v |= w[(wi + 1) * 64 + lane] << (32 - off);
+  return v & ((1u << BITS) - 1u);
+}
+
+// The fp16 bit pattern of 1024.0 in both halves, held in a vector register
+// (the kernels hide its value from the compiler once, so every field
+// extraction becomes a single v_and_or_b32 with the mask in a scalar register;
+// gfx9 VOP3 encodings cannot carry two literals).
+constexpr uint32_t kMagic1024 = 0x64006400u;
+
+__device__ __forceinline__ uint32_t magic_register() {
+  uint32_t mg = kMagic1024;
+  asm volatile("" : "+v"(mg));
+  return mg;
+}
+
+// Fast pair of slot s; in per-position mode the result is 2^p * deq.
+template <int BITS, bool POS>
 __device__ __forceinline__ h2_t fast_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
-                                          const Consts<BITS>& c) {
+                                          const Consts<BITS>& c, uint32_t mg) {
   using U = Unit<BITS>;
-  const h2_t m = as_h2(U::magic(w, s));
-  return (m - c.hz[U::pos(s)]) * c.hs[U::pos(s)];
+  const int i = U::pidx(U::pos(s));
+  const h2_t m = as_h2(U::magic(w, s, mg));
+  return (m - c.hz[i]) * c.hs[POS ? 0 : i];
 }
 
 // Where a unit's codes live in the row.  4-bit / 2-bit units are one run of
