@@ -39,7 +39,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix, published
 MALL_DEFEAT_BYTES = 1 << 30
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "qgemv_opt175b_3bit_traffic.json")
-GEMV_SOURCES = ["gemv.hip", "unit_decode.h", "common.h"]
+GEMV_SOURCES = ["gemv.hip", "gemv3.hip", "gemv_kernel.h", "unit_decode.h", "common.h"]
 
 
 def log(msg: str) -> None:

@@ -60,6 +60,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the 64 lanes with DPP lane permutations (no LDS traffic): pairs,
+// quads, half rows, rows of 16, then the row broadcasts fold rows 0+1 into
+// row 1, 2+3 into row 3 and finally everything into row 3.  Every lane gets
+// the total (read from lane 63).
+#define LOWBIT_DPP(v, ctrl, rmask)                                                     \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), \
+                                                        ctrl, rmask, 0xf, false))
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += LOWBIT_DPP(v, 0xb1, 0xf);   // quad_perm [1,0,3,2]
+  v += LOWBIT_DPP(v, 0x4e, 0xf);   // quad_perm [2,3,0,1]
+  v += LOWBIT_DPP(v, 0x141, 0xf);  // row_half_mirror
+  v += LOWBIT_DPP(v, 0x140, 0xf);  // row_mirror
+  v += LOWBIT_DPP(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  v += LOWBIT_DPP(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+#undef LOWBIT_DPP
+
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
@@ -74,5 +93,9 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Host side: compute-unit count of the current device, cached per device.
 int device_cu_count();
+
+// Host side: how many workgroups of `kernel` (block size, dynamic LDS) fit
+// on one CU at once (occupancy query, cached per kernel and shape; >= 1).
+int resident_blocks(const void* kernel, int block, size_t lds);
 
 }  // namespace lowbit

@@ -1,4 +1,4 @@
-// gemv_kernel.h -- fused dequantize + matrix-vector product, batch 1..15, on the VALU.
+// gemv_kernel.h -- fused dequantize + matrix-vector product, small batches, on the VALU.
 //
 // y[b][n] = sum_k x[b][k] * deq(packed[n])[k], with deq the exact fp16 value
 // fp16_rne((q - z) * s) of min-max RTN.  The weights stay low-bit in HBM and
@@ -9,18 +9,24 @@
 // quantization, "Quantization modes", weight_only_quant).
 //
 // Work layout on gfx950:
-//  - a workgroup is 4 waves; x (all B rows, all K) is staged once per
+//  - a workgroup is WAVES waves; x (all B rows, all K) is staged once per
 //    workgroup into LDS, already in the slot order the decode produces;
 //  - each wave owns R consecutive weight rows at a time ("tile"); lane l owns
 //    units l, l+64, ... of each row, so one load instruction of the wave
 //    reads 1 KiB (2/4-bit) or 768 B (3-bit) of contiguous packed words;
+//  - loads are buffer loads with the streaming (slc) cache policy, which
+//    measurably raises the HBM read rate on MI355X for data read once,
+//    through a per-row resource descriptor whose size
+//    is the row's byte count: lanes past the end of the row read zeros
+//    instead of touching the next row (the range check applies to the vector
+//    offset, so the K step is added there);
 //  - the wave walks a flat sequence of (tile, K step) iterations, loading the
 //    next iteration's words (two register buffers) while decoding the
 //    current one, so HBM reads stay in flight across tile boundaries;
 //  - v_dot2_f32_f16 accumulates x * deq in fp32; at the end of a tile the 64
-//    lanes are summed across the wave.
+//    lanes are summed with DPP permutations;
 //  - one group per row: the row's constants are wave-uniform (scalar
-//    registers); grouped rows take per-lane constants and "per-position"
+//    registers); grouped rows take per-lane constants and per-position
 //    accumulation (see unit_decode.h), which keeps the fast decode exact for
 //    every normal scale.
 #pragma once
@@ -33,9 +39,19 @@ namespace lowbit {
 
 namespace gemv_detail {
 
-constexpr int kGemvWaves = 4;
-constexpr int kGemvThreads = kGemvWaves * kWave;
-constexpr size_t kGemvLdsBudget = 64 * 1024;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr size_t kLdsBudget = 64 * 1024;
+constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
+constexpr int kSlc = 2;  // buffer-load cache policy for the weights: streaming
+
+typedef uint32_t u3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferDword3);
+}
 
 // Unit a lane handles in K step j.
 template <int BITS>
@@ -62,6 +78,12 @@ constexpr int codes_per_step() {
   return 64 * Unit<BITS>::CODES;
 }
 
+// Bytes of packed words one K step covers (64 lanes).
+template <int BITS>
+constexpr int bytes_per_step() {
+  return codes_per_step<BITS>() * BITS / 8;
+}
+
 // 2^-p of accumulator index i in per-position mode.
 template <int BITS>
 __device__ __forceinline__ float pos_scale(int i) {
@@ -69,12 +91,89 @@ __device__ __forceinline__ float pos_scale(int i) {
   return 1.0f / (float)(1 << p);
 }
 
+// Order in which the matrix-vector kernel groups a unit's slots into quads
+// (four fp16 pairs = one 16-byte activation entry = one MFMA operand).
+// Scaled mode keeps the natural order; per-position mode puts slots of equal
+// bit position together, so that every quad feeds a single accumulator.
+template <int BITS, bool POS>
+__host__ __device__ constexpr int quad_slot(int t, int e) {
+  if constexpr (POS && BITS == 4) {
+    constexpr int tab[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
+    return tab[4 * t + e];
+  } else if constexpr (POS && BITS == 2) {
+    constexpr int tab[32] = {0, 5, 8, 13, 16, 21, 24, 29, 1, 6, 9, 14, 17, 22, 25, 30,
+                             2, 7, 10, 15, 18, 23, 26, 31, 3, 11, 19, 27, 4, 12, 20, 28};
+    return tab[4 * t + e];
+  } else {
+    return 4 * t + e;
+  }
+}
+
+// Quad and element holding slot s (inverse of quad_slot).
+template <int BITS, bool POS>
+__host__ __device__ constexpr int slot_quad_elem(int s) {
+  for (int t = 0; t < Unit<BITS>::QUADS; ++t)
+    for (int e = 0; e < 4; ++e)
+      if (quad_slot<BITS, POS>(t, e) == s) return 4 * t + e;
+  return -1;
+}
+
+template <int BITS, bool POS>
+constexpr bool quads_single_position() {
+  using U = Unit<BITS>;
+  bool seen[U::SLOTS] = {};
+  for (int t = 0; t < U::QUADS; ++t)
+    for (int e = 0; e < 4; ++e) {
+      const int s = quad_slot<BITS, POS>(t, e);
+      if (s < 0 || s >= U::SLOTS || seen[s]) return false;
+      seen[s] = true;
+      if (POS && U::pos(s) != U::pos(quad_slot<BITS, POS>(t, 0))) return false;
+    }
+  return true;
+}
+static_assert(quads_single_position<4, false>() && quads_single_position<4, true>() &&
+                  quads_single_position<2, false>() && quads_single_position<2, true>() &&
+                  quads_single_position<3, false>(),
+              "quad orders must be permutations of the slots, one bit position per quad");
+
+// Activation entry of quad t with slots in any order: eight 2-byte gathers.
+template <int BITS, bool POS>
+__device__ __forceinline__ uint4 x_entry_ordered(const uint16_t* __restrict__ xrow,
+                                                 const UnitRef& u, int t) {
+  using U = Unit<BITS>;
+  if constexpr (!POS) {
+    return x_entry<BITS>(xrow, u, t, true);
+  } else {
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int s = quad_slot<BITS, POS>(t, e);
+      const int cl = U::lo(s), ch = U::hi(s);
+      const bool vl = BITS == 3 ? (cl < 32 ? u.va : u.vb) : u.va;
+      const bool vh = BITS == 3 ? (ch < 32 ? u.va : u.vb) : u.va;
+      const uint32_t a = vl ? xrow[unit_k<BITS>(u, cl)] : 0u;
+      const uint32_t b = vh ? xrow[unit_k<BITS>(u, ch)] : 0u;
+      d[e] = a | (b << 16);
+    }
+    return make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// The diagonal element D[j][j] of a 16x16 MFMA accumulator that lane l
+// holds: lanes whose column (l % 16) falls in their row block 4*(l / 16)
+// .. +3 hold one diagonal element each (element l % 4); the others give 0.
+__device__ __forceinline__ float mfma_diag(const f4_t& d, int lane) {
+  const int e = lane & 3;
+  const float v = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+  return ((lane & 15) >> 2) == (lane >> 4) ? v : 0.0f;
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
 template <int BITS, int BB, int R, bool PERROW, bool SPLIT>
-__global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
+__global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
     uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift, int J, int Jfull) {
@@ -86,15 +185,27 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
   // scale/zero loads per row and unit: a 3-bit unit's two periods (lo / hi
   // halves) may sit in different groups, and so may a 2-bit unit's two periods
   constexpr int NL = (BITS == 3 && !PERROW) || (BITS == 2 && SPLIT) ? 2 : 1;
+  // Batch 1, one group per row: the multiply-accumulate runs on the matrix
+  // cores (grouped layouts keep v_dot2: their per-position accumulators would
+  // need one MFMA accumulator tile per bit position, which costs more
+  // registers than it saves).  Each lane
+  // puts its own 8 activations (A operand) and its own 8 dequantized weights
+  // (B operand) into v_mfma_f32_16x16x32_f16; the diagonal D[j][j] of the
+  // result is then the dot product over lanes j, j+16, j+32, j+48, and the
+  // VALU only decodes.  (Off-diagonal entries mix lanes and are ignored.)
+  constexpr bool MD = BB == 1 && PERROW;
   extern __shared__ uint4 xs[];                      // [J][Q][BB][64], then slow scratch
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t wpr = (int64_t)K * BITS / 32;
-  const int ntiles = (N + kGemvWaves * R - 1) / (kGemvWaves * R);
+  const uint32_t row_bytes = (uint32_t)K * BITS / 8;
+  const int ntiles = (N + kWaves * R - 1) / (kWaves * R);
   const int mytiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1
                                                : 0;
   const int total = mytiles * J;
+  // per-lane byte offsets of the lane's unit inside one K step
+  const uint32_t off_a = BITS == 3 ? 12u * lane : 16u * lane;
+  const uint32_t off_b = off_a + 768u;
 
   struct Buf {
     uint32_t w[R][W];
@@ -102,35 +213,31 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     int32_t z[R][NL];
   };
 
-  auto row_of = [&](int it, int r) {
-    const int k = it / J;
-    const int tile = (int)blockIdx.x + k * (int)gridDim.x;
-    const int n = (tile * kGemvWaves + wave) * R + r;
-    return n < N ? n : N - 1;
-  };
+  auto first_row = [&](int k) { return (((int)blockIdx.x + k * (int)gridDim.x) * kWaves + wave) * R; };
 
-  auto load = [&](int it, Buf& b) {
-    const int j = it % J;
-    UnitRef u = gemv_unit<BITS>(j, lane, K);
-    if (j >= Jfull) {  // past the end of the row: read unit 0 instead, masked later
-      if (!u.va) u.ka = 0;
-      if (!u.vb) u.kb = 0;
-    }
+  const auto srs = rsrc(scales, (uint32_t)min((int64_t)N * G * 2, (int64_t)0x7fffffff));
+  const auto zrs = rsrc(zeros, (uint32_t)min((int64_t)N * G * 4, (int64_t)0x7fffffff));
+  auto load = [&](int k, int j, Buf& b) {
+    const int n0 = first_row(k);
+    const uint32_t step = (uint32_t)j * bytes_per_step<BITS>();
+    const uint32_t va_off = off_a + step, vb_off = off_b + step;
+    UnitRef u;
+    if constexpr (!PERROW) u = gemv_unit<BITS>(j, lane, K);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = row_of(it, r);
-      const uint32_t* rowp = packed + (int64_t)n * wpr;
+      const int n = min(n0 + r, N - 1);
+      const auto rs = rsrc(packed + (int64_t)n * (row_bytes / 4), row_bytes);
       if constexpr (BITS == 3) {
-        const uint32_t* pa = rowp + 3 * (u.ka >> 5);
-        const uint32_t* pb = rowp + 3 * (u.kb >> 5);
-        b.w[r][0] = pa[0];
-        b.w[r][1] = pa[1];
-        b.w[r][2] = pa[2];
-        b.w[r][3] = pb[0];
-        b.w[r][4] = pb[1];
-        b.w[r][5] = pb[2];
+        const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, va_off, 0, kSlc);
+        const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, vb_off, 0, kSlc);
+        b.w[r][0] = va.x;
+        b.w[r][1] = va.y;
+        b.w[r][2] = va.z;
+        b.w[r][3] = vb.x;
+        b.w[r][4] = vb.y;
+        b.w[r][5] = vb.z;
       } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(rowp + (u.ka * BITS >> 5));
+        const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, va_off, 0, kSlc);
         b.w[r][0] = v.x;
         b.w[r][1] = v.y;
         b.w[r][2] = v.z;
@@ -138,8 +245,12 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
       }
       if constexpr (PERROW) {
         if (j == 0) {
-          b.s[r][0] = scales[n];
-          b.z[r][0] = zeros[n];
+          // vector (buffer) loads on purpose: a scalar load would share the
+          // lgkm counter with the LDS activation reads, and every wait on
+          // those would then also wait for this prefetch to come from HBM
+          const uint32_t nn = (uint32_t)n + 0u * (uint32_t)lane;
+          b.s[r][0] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * nn, 0, 0);
+          b.z[r][0] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(zrs, 4u * nn, 0, 0);
         }
       } else {
         const uint16_t* srow = scales + (int64_t)n * G;
@@ -147,7 +258,8 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
 #pragma unroll
         for (int c = 0; c < NL; ++c) {
           const int kk = BITS == 3 ? (c == 0 ? u.ka : u.kb) : u.ka + 32 * c;
-          const int g = group_of(kk, gsz, gshift);
+          const bool v = BITS == 3 ? (c == 0 ? u.va : u.vb) : u.va;
+          const int g = v ? group_of(kk, gsz, gshift) : 0;
           b.s[r][c] = srow[g];
           b.z[r][c] = zrow[g];
         }
@@ -158,11 +270,11 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
   // Prefetch the first iteration's weights before staging x, so the HBM
   // latency of the first loads overlaps the staging.
   Buf bufA, bufB;
-  if (total > 0) load(0, bufA);
+  if (total > 0) load(0, 0, bufA);
 
   const int entries = J * Q * BB * 64;
   uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(xs + entries);
-  for (int e = tid; e < entries; e += kGemvThreads) {
+  for (int e = tid; e < entries; e += kThreads) {
     const int l = e & 63;
     int rest = e >> 6;
     const int b = rest % BB;
@@ -170,7 +282,8 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     const int q = rest % Q;
     const int j = rest / Q;
     const UnitRef u = gemv_unit<BITS>(j, l, K);
-    xs[e] = x_entry<BITS>(x + (int64_t)b * K, u, q, true);
+    xs[e] = MD ? x_entry_ordered<BITS, POS>(x + (int64_t)b * K, u, q)
+               : x_entry<BITS>(x + (int64_t)b * K, u, q, true);
   }
   __syncthreads();
 
@@ -181,6 +294,11 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     for (int b = 0; b < BB; ++b)
 #pragma unroll
       for (int a = 0; a < NA; ++a) acc[r][b][a] = 0.0f;
+  f4_t dacc[R][MD ? NA : 1];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int a = 0; a < (MD ? NA : 1); ++a) dacc[r][a] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const uint32_t mg = magic_register();
   Consts<BITS> rowc[R];
@@ -188,8 +306,7 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
   int32_t rows_z[R];
   bool rowfast = true;
 
-  auto compute = [&](int it, Buf& b) {
-    const int j = it % J;
+  auto compute = [&](int k, int j, Buf& b) {
     const UnitRef u = gemv_unit<BITS>(j, lane, K);
     const bool tail = j >= Jfull;
     HalfParams hp[R][NC];
@@ -233,7 +350,26 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     }
 
     const uint4* xj = xs + (int64_t)j * Q * BB * 64 + lane;
-    if (fast) {
+    if (MD && fast) {
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+        const h8_t av = __builtin_bit_cast(h8_t, xj[t * 64]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          h2_t d[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = quad_slot<BITS, POS>(t, e);
+            const int c = NC == 1 ? 0 : U::cset(s);
+            d[e] = fast_pair<BITS, POS>(b.w[r], s, cc[r][c], mg);
+          }
+          const h8_t bv = __builtin_bit_cast(
+              h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
+          const int a = POS ? U::pidx(U::pos(quad_slot<BITS, POS>(t, 0))) : 0;
+          dacc[r][MD ? a : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, dacc[r][MD ? a : 0], 0, 0, 0);
+        }
+      }
+    } else if (!MD && fast) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         uint4 xq[BB];
@@ -273,7 +409,8 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
           const uint16_t dl = h.v_lo ? exact_deq(ql, h.z_lo, h_bits_to_f32(h.s_lo)) : (uint16_t)0;
           const uint16_t dh = h.v_hi ? exact_deq(qh, h.z_hi, h_bits_to_f32(h.s_hi)) : (uint16_t)0;
           const h2_t d = as_h2((uint32_t)dl | ((uint32_t)dh << 16));
-          const int q = s >> 2, e = s & 3;
+          const int qe = MD ? slot_quad_elem<BITS, POS>(s) : s;
+          const int q = qe >> 2, e = qe & 3;
 #pragma unroll
           for (int bb = 0; bb < BB; ++bb) {
             const uint32_t xv = xj32[((q * BB + bb) * 64 + lane) * 4 + e];
@@ -284,18 +421,23 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     }
 
     if (j == J - 1) {
-      const int k = it / J;
-      const int tile = (int)blockIdx.x + k * (int)gridDim.x;
+      const int n0 = first_row(k);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int n = (tile * kGemvWaves + wave) * R + r;
 #pragma unroll
         for (int bb = 0; bb < BB; ++bb) {
           float v = acc[r][bb][0];
 #pragma unroll
           for (int a = 1; a < NA; ++a) v += acc[r][bb][a] * pos_scale<BITS>(a);
-          v = wave_sum(v);
-          if (lane == 0 && n < N) y[(int64_t)bb * N + n] = f32_to_h_bits(v);
+          if constexpr (MD) {
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+              v += mfma_diag(dacc[r][a], lane) * pos_scale<BITS>(a);
+              dacc[r][a] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
+          v = wave_sum_dpp(v);
+          if (lane == 0 && n0 + r < N) y[(int64_t)bb * N + n0 + r] = f32_to_h_bits(v);
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[r][bb][a] = 0.0f;
         }
@@ -303,14 +445,30 @@ __global__ __launch_bounds__(kGemvThreads) void qgemv_kernel(
     }
   };
 
+  // Two-deep software pipeline over the flat (tile k, K step j) sequence:
+  // the loads of iteration i+1 are issued before iteration i is decoded.
+  int ck = 0, cj = 0;  // iteration being computed
+  int lk = 0, lj = 0;  // iteration most recently loaded
+  auto advance = [&](int& k, int& j) {
+    if (++j == J) {
+      j = 0;
+      ++k;
+    }
+  };
   int it = 0;
   for (; it + 1 < total; it += 2) {
-    load(it + 1, bufB);
-    compute(it, bufA);
-    if (it + 2 < total) load(it + 2, bufA);
-    compute(it + 1, bufB);
+    advance(lk, lj);
+    load(lk, lj, bufB);
+    compute(ck, cj, bufA);
+    advance(ck, cj);
+    if (it + 2 < total) {
+      advance(lk, lj);
+      load(lk, lj, bufA);
+    }
+    compute(ck, cj, bufB);
+    advance(ck, cj);
   }
-  if (it < total) compute(it, bufA);
+  if (it < total) compute(ck, cj, bufA);
 }
 
 template <int BITS, int BB, bool PERROW, bool SPLIT>
@@ -321,15 +479,15 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   const int J = (K + codes_per_step<BITS>() - 1) / codes_per_step<BITS>();
   const int Jfull = K / codes_per_step<BITS>();
   const size_t lds = (size_t)J * Unit<BITS>::QUADS * BB * 64 * sizeof(uint4) +
-                     (size_t)kGemvWaves * Unit<BITS>::WORDS * 64 * sizeof(uint32_t);
-  if (lds > kGemvLdsBudget) return hipErrorNotSupported;
-  const int ntiles = (N + kGemvWaves * R - 1) / (kGemvWaves * R);
-  int per_cu = (int)(160 * 1024 / (lds + 1024));
-  per_cu = per_cu < 1 ? 1 : per_cu > 4 ? 4 : per_cu;
+                     (size_t)kWaves * Unit<BITS>::WORDS * 64 * sizeof(uint32_t);
+  if (lds > kLdsBudget) return hipErrorNotSupported;
+  const int ntiles = (N + kWaves * R - 1) / (kWaves * R);
+  const auto kern = qgemv_kernel<BITS, BB, R, PERROW, SPLIT>;
+  const int per_cu = resident_blocks(reinterpret_cast<const void*>(kern), kThreads, lds);
   const int cap = device_cu_count() * per_cu;
   const int grid = ntiles < cap ? ntiles : cap;
-  hipLaunchKernelGGL((qgemv_kernel<BITS, BB, R, PERROW, SPLIT>), dim3(grid), dim3(kGemvThreads),
-                     lds, stream, x, packed, scales, zeros, y, N, K, G, gsz, gshift, J, Jfull);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, x, packed, scales, zeros, y, N,
+                     K, G, gsz, gshift, J, Jfull);
   return hipGetLastError();
 }
 
