@@ -28,29 +28,20 @@ int device_cu_count() {
   return cache[dev];
 }
 
-int resident_blocks(const void* kernel, int block, size_t lds) {
-  struct Key {
-    const void* k;
-    int block;
-    size_t lds;
-    int dev;
-    int val;
-  };
+size_t device_lds_per_block() {
   static std::mutex mu;
-  static Key cache[256];
-  static int used = 0;
+  static size_t cache[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
   std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (cache[i].k == kernel && cache[i].block == block && cache[i].lds == lds &&
-        cache[i].dev == dev)
-      return cache[i].val;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds) != hipSuccess || n < 1)
-    n = 1;
-  if (used < 256) cache[used++] = Key{kernel, block, lds, dev, n};
-  return n;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v <= 0)
+      v = 64 * 1024;
+    cache[dev] = (size_t)v;
+  }
+  return cache[dev];
 }
 
 }  // namespace lowbit

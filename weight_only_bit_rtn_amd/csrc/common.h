@@ -94,8 +94,8 @@ __device__ __forceinline__ float wave_max(float v) {
 // Host side: compute-unit count of the current device, cached per device.
 int device_cu_count();
 
-// Host side: how many workgroups of `kernel` (block size, dynamic LDS) fit
-// on one CU at once (occupancy query, cached per kernel and shape; >= 1).
-int resident_blocks(const void* kernel, int block, size_t lds);
+// Host side: the largest LDS allocation one workgroup may make on the current
+// device (bytes, cached per device).
+size_t device_lds_per_block();
 
 }  // namespace lowbit

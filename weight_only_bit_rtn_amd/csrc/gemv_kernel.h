@@ -9,22 +9,30 @@
 // quantization, "Quantization modes", weight_only_quant).
 //
 // Work layout on gfx950:
-//  - a workgroup is WAVES waves; x (all B rows, all K) is staged once per
-//    workgroup into LDS, already in the slot order the decode produces;
-//  - each wave owns R consecutive weight rows at a time ("tile"); lane l owns
-//    units l, l+64, ... of each row, so one load instruction of the wave
-//    reads 1 KiB (2/4-bit) or 768 B (3-bit) of contiguous packed words;
-//  - loads are buffer loads with the streaming (slc) cache policy, which
-//    measurably raises the HBM read rate on MI355X for data read once,
-//    through a per-row resource descriptor whose size
-//    is the row's byte count: lanes past the end of the row read zeros
-//    instead of touching the next row (the range check applies to the vector
-//    offset, so the K step is added there);
-//  - the wave walks a flat sequence of (tile, K step) iterations, loading the
+//  - one persistent workgroup of 16 waves per CU (the kernel claims the
+//    register budget of four waves per SIMD, so two never share a CU); x
+//    (all B rows, all K) is staged once per workgroup into LDS, already in
+//    the slot order the decode produces;
+//  - each workgroup owns an equal, contiguous share of the row tiles (R rows
+//    each); its waves draw work items -- a tile, or a K chunk of a tile when
+//    there are few tiles per wave -- from a counter in LDS, so a wave that
+//    the issue arbiter favours simply takes more items and all waves finish
+//    together instead of the youngest ones running alone at the end;
+//  - lane l owns units l, l+64, ... of each row, so one load instruction of
+//    the wave reads 1 KiB (2/4-bit) or 768 B (3-bit) of contiguous packed
+//    words; loads are buffer loads with the streaming (slc) cache policy,
+//    which measurably raises the HBM read rate on MI355X for data read once,
+//    through a per-row resource descriptor whose size is the row's byte
+//    count: lanes past the end of the row read zeros instead of touching the
+//    next row (the range check applies to the vector offset, so the K step is
+//    added there);
+//  - the wave walks a flat sequence of (item, K step) iterations, loading the
 //    next iteration's words (two register buffers) while decoding the
-//    current one, so HBM reads stay in flight across tile boundaries;
-//  - v_dot2_f32_f16 accumulates x * deq in fp32; at the end of a tile the 64
-//    lanes are summed with DPP permutations;
+//    current one, so HBM reads stay in flight across item boundaries;
+//  - batch 1 with one group per row multiplies on the matrix cores (see
+//    below); otherwise v_dot2_f32_f16 accumulates x * deq in fp32; at the end
+//    of an item the 64 lanes are summed with DPP permutations into a partial
+//    sum in LDS, and the workgroup writes y with coalesced stores;
 //  - one group per row: the row's constants are wave-uniform (scalar
 //    registers); grouped rows take per-lane constants and per-position
 //    accumulation (see unit_decode.h), which keeps the fast decode exact for
@@ -39,9 +47,11 @@ namespace lowbit {
 
 namespace gemv_detail {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;                 // one 1024-thread workgroup per CU
 constexpr int kThreads = kWaves * kWave;
-constexpr size_t kLdsBudget = 64 * 1024;
+constexpr size_t kLdsBudget = 160 * 1024;   // gfx950 LDS per CU
+constexpr int kPartMax = 4096;              // fp32 partial sums per round
+constexpr int kItemsPerWave = 4;            // target work items per wave
 constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
 constexpr int kSlc = 2;  // buffer-load cache policy for the weights: streaming
 
@@ -172,11 +182,25 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
+// One work item: R consecutive rows (a "tile") of this workgroup's current
+// round, over K steps [jb, je) (K chunk c of 2^lgjc), with the buffer
+// descriptors of its rows.
+template <int R>
+struct Item {
+  int i;       // item number; i >= nit means no more work
+  int tl;      // tile index inside the round
+  int c;       // K chunk
+  int jb, je;  // K steps of the chunk
+  int j;       // K step being loaded / computed
+  __amdgpu_buffer_rsrc_t rs[R];
+};
+
 template <int BITS, int BB, int R, bool PERROW, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
-    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift, int J, int Jfull) {
+    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift, int J, int lgjc,
+    int RT) {
   using U = Unit<BITS>;
   constexpr int Q = U::QUADS, W = U::WORDS;
   constexpr bool POS = !PERROW;                      // per-position accumulation
@@ -194,18 +218,35 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   // result is then the dot product over lanes j, j+16, j+32, j+48, and the
   // VALU only decodes.  (Off-diagonal entries mix lanes and are ignored.)
   constexpr bool MD = BB == 1 && PERROW;
-  extern __shared__ uint4 xs[];                      // [J][Q][BB][64], then slow scratch
+  // LDS: activations [J][Q][BB][64] | per-wave slow-path scratch |
+  //      partial sums [RT * R rows][BB][JC] | work counter
+  extern __shared__ uint4 xs[];
+
+  // Claim the whole register budget of four waves per SIMD, so that two of
+  // these 16-wave workgroups can never share a CU (the work split below
+  // assumes one workgroup per CU).
+  asm volatile("" ::: "v127");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t row_bytes = (uint32_t)K * BITS / 8;
-  const int ntiles = (N + kWaves * R - 1) / (kWaves * R);
-  const int mytiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1
-                                               : 0;
-  const int total = mytiles * J;
   // per-lane byte offsets of the lane's unit inside one K step
   const uint32_t off_a = BITS == 3 ? 12u * lane : 16u * lane;
   const uint32_t off_b = off_a + 768u;
+
+  // This workgroup's tiles: an equal share of all of them, in rounds of at
+  // most RT tiles (bounded by the partial-sum space).
+  const int T = (N + R - 1) / R;
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int tbase = T / nwg, textra = T % nwg;
+  const int t0 = wg * tbase + min(wg, textra);
+  const int t1 = t0 + tbase + (wg < textra ? 1 : 0);
+
+  const int JC = 1 << lgjc;
+  const int entries = J * Q * BB * 64;
+  uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(xs + entries);
+  float* part = reinterpret_cast<float*>(slow_scratch + kWaves * W * 64);
+  int* counter = reinterpret_cast<int*>(part + RT * R * BB * JC);
 
   struct Buf {
     uint32_t w[R][W];
@@ -213,38 +254,53 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     int32_t z[R][NL];
   };
 
-  auto first_row = [&](int k) { return (((int)blockIdx.x + k * (int)gridDim.x) * kWaves + wave) * R; };
-
   const auto srs = rsrc(scales, (uint32_t)min((int64_t)N * G * 2, (int64_t)0x7fffffff));
   const auto zrs = rsrc(zeros, (uint32_t)min((int64_t)N * G * 4, (int64_t)0x7fffffff));
-  auto load = [&](int k, int j, Buf& b) {
-    const int n0 = first_row(k);
+  int rt0 = t0;  // first tile of the current round
+  int nit = 0;   // items of the current round
+
+  auto make_item = [&](int i) {
+    Item<R> t;
+    t.i = i;
+    t.tl = i >> lgjc;
+    t.c = i & (JC - 1);
+    t.jb = (t.c * J) >> lgjc;
+    t.je = ((t.c + 1) * J) >> lgjc;
+    t.j = t.jb;
+    const int n0 = (rt0 + t.tl) * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      t.rs[r] = rsrc(packed + (int64_t)min(n0 + r, N - 1) * (row_bytes / 4), row_bytes);
+    return t;
+  };
+  // Next (item, K step) of this wave: the next step of the same item, else a
+  // fresh item from the workgroup's counter (an LDS atomic by lane 0).
+  auto next_of = [&](const Item<R>& t) {
+    if (t.j + 1 < t.je) {
+      Item<R> u = t;
+      ++u.j;
+      return u;
+    }
+    int v = 0;
+    if (lane == 0) v = atomicAdd(counter, 1);
+    v = __builtin_amdgcn_readfirstlane(v);
+    return make_item(v < nit ? v : nit);
+  };
+
+  auto load = [&](const Item<R>& t, Buf& b) {
+    const int n0 = (rt0 + t.tl) * R;
+    const int j = t.j;
     const uint32_t step = (uint32_t)j * bytes_per_step<BITS>();
     const uint32_t va_off = off_a + step, vb_off = off_b + step;
     UnitRef u;
     if constexpr (!PERROW) u = gemv_unit<BITS>(j, lane, K);
+    // scale / zero loads first: a wait for this step's words then also
+    // covers them, whatever the number of loads issued after
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = min(n0 + r, N - 1);
-      const auto rs = rsrc(packed + (int64_t)n * (row_bytes / 4), row_bytes);
-      if constexpr (BITS == 3) {
-        const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, va_off, 0, kSlc);
-        const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, vb_off, 0, kSlc);
-        b.w[r][0] = va.x;
-        b.w[r][1] = va.y;
-        b.w[r][2] = va.z;
-        b.w[r][3] = vb.x;
-        b.w[r][4] = vb.y;
-        b.w[r][5] = vb.z;
-      } else {
-        const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, va_off, 0, kSlc);
-        b.w[r][0] = v.x;
-        b.w[r][1] = v.y;
-        b.w[r][2] = v.z;
-        b.w[r][3] = v.w;
-      }
       if constexpr (PERROW) {
-        if (j == 0) {
+        if (j == t.jb) {
           // vector (buffer) loads on purpose: a scalar load would share the
           // lgkm counter with the LDS activation reads, and every wait on
           // those would then also wait for this prefetch to come from HBM
@@ -265,27 +321,27 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         }
       }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const auto rs = t.rs[r];
+      if constexpr (BITS == 3) {
+        const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, va_off, 0, kSlc);
+        const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, vb_off, 0, kSlc);
+        b.w[r][0] = va.x;
+        b.w[r][1] = va.y;
+        b.w[r][2] = va.z;
+        b.w[r][3] = vb.x;
+        b.w[r][4] = vb.y;
+        b.w[r][5] = vb.z;
+      } else {
+        const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, va_off, 0, kSlc);
+        b.w[r][0] = v.x;
+        b.w[r][1] = v.y;
+        b.w[r][2] = v.z;
+        b.w[r][3] = v.w;
+      }
+    }
   };
-
-  // Prefetch the first iteration's weights before staging x, so the HBM
-  // latency of the first loads overlaps the staging.
-  Buf bufA, bufB;
-  if (total > 0) load(0, 0, bufA);
-
-  const int entries = J * Q * BB * 64;
-  uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(xs + entries);
-  for (int e = tid; e < entries; e += kThreads) {
-    const int l = e & 63;
-    int rest = e >> 6;
-    const int b = rest % BB;
-    rest /= BB;
-    const int q = rest % Q;
-    const int j = rest / Q;
-    const UnitRef u = gemv_unit<BITS>(j, l, K);
-    xs[e] = MD ? x_entry_ordered<BITS, POS>(x + (int64_t)b * K, u, q)
-               : x_entry<BITS>(x + (int64_t)b * K, u, q, true);
-  }
-  __syncthreads();
 
   float acc[R][BB][NA];
 #pragma unroll
@@ -306,14 +362,14 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   int32_t rows_z[R];
   bool rowfast = true;
 
-  auto compute = [&](int k, int j, Buf& b) {
+  auto compute = [&](const Item<R>& t, Buf& b) {
+    const int j = t.j;
     const UnitRef u = gemv_unit<BITS>(j, lane, K);
-    const bool tail = j >= Jfull;
     HalfParams hp[R][NC];
     Consts<BITS> cc[R][NC];
     bool fast = true;
     if constexpr (PERROW) {
-      if (j == 0) {
+      if (j == t.jb) {
         rowfast = true;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -321,6 +377,11 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
           rows_z[r] = (int32_t)uniform((uint32_t)b.z[r][0]);
           HalfParams h{rows_s[r], rows_s[r], rows_z[r], rows_z[r], true, true};
           rowfast &= make_consts<BITS, false>(h, rowc[r]);
+          // Positions past the end of the row (last K step of a ragged row)
+          // are decoded from zero words without masking: their activations
+          // are staged as zeros, so only a finite decode is needed there,
+          // which |q - z| * s <= 15 * s < 65504 guarantees.
+          rowfast &= rows_s[r] < 0x6C00u;  // s < 4096
 #pragma unroll
           for (int i = 0; i < U::NPOS; ++i) {
             rowc[r].hz[i] = as_h2(uniform(as_u32(rowc[r].hz[i])));
@@ -329,11 +390,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        hp[r][0] = HalfParams{rows_s[r], rows_s[r], rows_z[r], rows_z[r], u.va, u.vb};
-        cc[r][0] = rowc[r];
-        if (tail) mask_consts<BITS, false>(cc[r][0], u.va, u.vb);
-      }
+      for (int r = 0; r < R; ++r) cc[r][0] = rowc[r];
       fast = rowfast;
     } else {
 #pragma unroll
@@ -351,22 +408,27 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
 
     const uint4* xj = xs + (int64_t)j * Q * BB * 64 + lane;
     if (MD && fast) {
+      // all activation quads of the step first: one LDS wait per step
+      uint4 xq[Q];
 #pragma unroll
-      for (int t = 0; t < Q; ++t) {
-        const h8_t av = __builtin_bit_cast(h8_t, xj[t * 64]);
+      for (int q = 0; q < Q; ++q) xq[q] = xj[q * 64];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const h8_t av = __builtin_bit_cast(h8_t, xq[q]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           h2_t d[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int s = quad_slot<BITS, POS>(t, e);
+            const int s = quad_slot<BITS, POS>(q, e);
             const int c = NC == 1 ? 0 : U::cset(s);
             d[e] = fast_pair<BITS, POS>(b.w[r], s, cc[r][c], mg);
           }
           const h8_t bv = __builtin_bit_cast(
               h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
-          const int a = POS ? U::pidx(U::pos(quad_slot<BITS, POS>(t, 0))) : 0;
-          dacc[r][MD ? a : 0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, dacc[r][MD ? a : 0], 0, 0, 0);
+          const int a = POS ? U::pidx(U::pos(quad_slot<BITS, POS>(q, 0))) : 0;
+          dacc[r][MD ? a : 0] =
+              __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, dacc[r][MD ? a : 0], 0, 0, 0);
         }
       }
     } else if (!MD && fast) {
@@ -403,7 +465,9 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
 #pragma unroll 1
         for (int s = 0; s < U::SLOTS; ++s) {
           const int c = NC == 1 ? 0 : U::cset(s);
-          const HalfParams h = c == 0 ? hp[r][0] : hp[r][NC - 1];
+          const HalfParams h =
+              PERROW ? HalfParams{rows_s[r], rows_s[r], rows_z[r], rows_z[r], u.va, u.vb}
+                     : c == 0 ? hp[r][0] : hp[r][NC - 1];
           const int ql = (int)unit_code_lds<BITS>(wsc, lane, U::lo(s));
           const int qh = (int)unit_code_lds<BITS>(wsc, lane, U::hi(s));
           const uint16_t dl = h.v_lo ? exact_deq(ql, h.z_lo, h_bits_to_f32(h.s_lo)) : (uint16_t)0;
@@ -420,8 +484,8 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
       }
     }
 
-    if (j == J - 1) {
-      const int n0 = first_row(k);
+    if (j == t.je - 1) {
+      // end of the item: one partial sum per (row, batch row) into LDS
 #pragma unroll
       for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -437,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
             }
           }
           v = wave_sum_dpp(v);
-          if (lane == 0 && n0 + r < N) y[(int64_t)bb * N + n0 + r] = f32_to_h_bits(v);
+          if (lane == 0) part[((t.tl * R + r) * BB + bb) * JC + t.c] = v;
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[r][bb][a] = 0.0f;
         }
@@ -445,49 +509,96 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     }
   };
 
-  // Two-deep software pipeline over the flat (tile k, K step j) sequence:
-  // the loads of iteration i+1 are issued before iteration i is decoded.
-  int ck = 0, cj = 0;  // iteration being computed
-  int lk = 0, lj = 0;  // iteration most recently loaded
-  auto advance = [&](int& k, int& j) {
-    if (++j == J) {
-      j = 0;
-      ++k;
+  Buf bufA, bufB;
+  for (bool first = true; rt0 < t1; rt0 += RT, first = false) {
+    const int ntl = min(RT, t1 - rt0);
+    nit = ntl * JC;
+    // items 0 .. kWaves-1 go to waves 0 .. kWaves-1; the rest are claimed
+    Item<R> cur = make_item(wave < nit ? wave : nit);
+    // the first weights are requested before the activations are staged, so
+    // their HBM latency overlaps the staging
+    if (cur.i < nit) load(cur, bufA);
+    if (tid == 0) *counter = kWaves;
+    if (first) {
+      for (int e = tid; e < entries; e += kThreads) {
+        const int l = e & 63;
+        int rest = e >> 6;
+        const int b = rest % BB;
+        rest /= BB;
+        const int q = rest % Q;
+        const int jj = rest / Q;
+        const UnitRef uu = gemv_unit<BITS>(jj, l, K);
+        xs[e] = MD ? x_entry_ordered<BITS, POS>(x + (int64_t)b * K, uu, q)
+                   : x_entry<BITS>(x + (int64_t)b * K, uu, q, true);
+      }
     }
-  };
-  int it = 0;
-  for (; it + 1 < total; it += 2) {
-    advance(lk, lj);
-    load(lk, lj, bufB);
-    compute(ck, cj, bufA);
-    advance(ck, cj);
-    if (it + 2 < total) {
-      advance(lk, lj);
-      load(lk, lj, bufA);
+    __syncthreads();
+
+    // Two-deep software pipeline: the loads of the next (item, K step) are
+    // issued before the current one is decoded.
+    // The prefetch is issued even past the last item (its rows are clamped
+    // to valid memory and the words are never used): an unconditional load
+    // keeps the wait before each decode at "all but the newest loads done".
+    while (cur.i < nit) {
+      Item<R> nx = next_of(cur);
+      load(nx, bufB);
+      compute(cur, bufA);
+      cur = nx;
+      if (cur.i >= nit) break;
+      nx = next_of(cur);
+      load(nx, bufA);
+      compute(cur, bufB);
+      cur = nx;
     }
-    compute(ck, cj, bufB);
-    advance(ck, cj);
+    __syncthreads();
+
+    // the round's outputs: sum the K chunks in order, coalesced stores
+    const int row0 = rt0 * R;
+    const int nrows = min((rt0 + ntl) * R, N) - row0;
+    for (int e = tid; e < nrows * BB; e += kThreads) {
+      const int bb = e / nrows, rr = e - bb * nrows;
+      const float* pp = part + (rr * BB + bb) * JC;
+      float v = 0.0f;
+      for (int c = 0; c < JC; ++c) v += pp[c];
+      y[(int64_t)bb * N + row0 + rr] = f32_to_h_bits(v);
+    }
+    __syncthreads();  // partial sums and counter are reused by the next round
   }
-  if (it < total) compute(ck, cj, bufA);
 }
 
 template <int BITS, int BB, bool PERROW, bool SPLIT>
 hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
-  constexpr int R = BB <= 4 ? 2 : 1;
+  using U = Unit<BITS>;
+  // two rows per wave where the accumulators leave room for a second row
+  constexpr int NA = PERROW ? 1 : U::NPOS;
+  constexpr int R = (BB <= 4 && BB * NA <= 16) ? 2 : 1;
   const int J = (K + codes_per_step<BITS>() - 1) / codes_per_step<BITS>();
-  const int Jfull = K / codes_per_step<BITS>();
-  const size_t lds = (size_t)J * Unit<BITS>::QUADS * BB * 64 * sizeof(uint4) +
-                     (size_t)kWaves * Unit<BITS>::WORDS * 64 * sizeof(uint32_t);
-  if (lds > kLdsBudget) return hipErrorNotSupported;
-  const int ntiles = (N + kWaves * R - 1) / (kWaves * R);
+  const int T = (N + R - 1) / R;
+  const int cus = device_cu_count();
+  const int nwg = T < cus ? T : cus;
+  const int tiles_per_wg = (T + nwg - 1) / nwg;
+  // K chunks per tile (a power of two, at most J): enough work items that
+  // every wave draws several
+  int lgjc = 0;
+  while ((tiles_per_wg << lgjc) < kItemsPerWave * kWaves && (2 << lgjc) <= J) ++lgjc;
+  const int JC = 1 << lgjc;
+  int RT = kPartMax / (R * BB * JC);
+  if (RT > tiles_per_wg) RT = tiles_per_wg;
+  if (RT < 1) return hipErrorNotSupported;
+  const size_t lds = (size_t)J * U::QUADS * BB * 64 * sizeof(uint4) +
+                     (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) +
+                     (size_t)RT * R * BB * JC * sizeof(float) + 16;
+  if (lds > device_lds_per_block() || lds > kLdsBudget) return hipErrorNotSupported;
   const auto kern = qgemv_kernel<BITS, BB, R, PERROW, SPLIT>;
-  const int per_cu = resident_blocks(reinterpret_cast<const void*>(kern), kThreads, lds);
-  const int cap = device_cu_count() * per_cu;
-  const int grid = ntiles < cap ? ntiles : cap;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, x, packed, scales, zeros, y, N,
-                     K, G, gsz, gshift, J, Jfull);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), lds, stream, x, packed, scales, zeros, y, N,
+                     K, G, gsz, gshift, J, lgjc, RT);
   return hipGetLastError();
 }
 

@@ -207,16 +207,6 @@ __device__ __forceinline__ bool make_consts(const HalfParams& hp, Consts<BITS>& 
   return fl && fh;
 }
 
-// Zero the scales of invalid halves (units past the end of the row).
-template <int BITS, bool POS>
-__device__ __forceinline__ void mask_consts(Consts<BITS>& c, bool v_lo, bool v_hi) {
-  using U = Unit<BITS>;
-  constexpr int n = POS ? 1 : U::NPOS;
-  const uint32_t keep = (v_lo ? 0x0000ffffu : 0u) | (v_hi ? 0xffff0000u : 0u);
-#pragma unroll
-  for (int i = 0; i < n; ++i) c.hs[i] = as_h2(as_u32(c.hs[i]) & keep);
-}
-
 // fp16_rne((q - z) * s) for any code, zero point and scale: the product is
 // formed in fp32 and rounded to odd (its last bit records inexactness), which
 // makes the following fp32 -> fp16 rounding the correctly rounded result
