@@ -12,10 +12,10 @@ packed weights (>= 1 GB in total).
 
 value = algorithmic bytes of the step (packed words + scales + zeros + x + y)
 over the wall time of the timed steps; roofline.achieved = the same bytes per
-GEMV launch over the launches' average duration measured with HIP events on
-the launch stream.  The quantizer (lowbit_quantize_rtn) and the matrix-core
-product (lowbit_qgemm, Llama-70B MLP shape at batch 16/32/64) are measured in
-the same run as separate stages.  The CPU baseline times the C oracle's
+GEMV launch over the average launch duration, from HIP events recorded on the
+launch stream around the timed region (elapsed / launches).  The quantizer
+(lowbit_quantize_rtn) and the matrix-core product (lowbit_qgemm, Llama-70B MLP
+shape at batch 16/32/64) are measured in the same run as separate stages.  The CPU baseline times the C oracle's
 dequantize + fp64 product on a sample of rows of the same layers.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
@@ -215,6 +215,34 @@ def load_traffic(avg_bytes_per_launch: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def counter_pass(lw, torch, layers, stream: int) -> int:
+    """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes: three GEMV
+    launches per layer (distinct weight copies), then three plain device-to-device
+    copies of COPY_BYTES whose counter readings calibrate the bytes per count."""
+    preps = [Prepared(lw, torch, L, 3) for L in layers]
+    for p in preps:
+        del p.w
+    torch.cuda.synchronize()
+    for p in preps:
+        for i in range(3):
+            run_product(lw, p, 1, i, stream, "qgemv")
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    per_launch = {p.layer.name: product_bytes(p.layer.N, p.layer.K, p.layer.bits,
+                                              p.layer.group_size, 1) for p in preps}
+    print(json.dumps({"counter_pass": True, "copy_bytes": COPY_BYTES,
+                      "algorithmic_bytes_per_launch": per_launch}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +251,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="for rocprofv3 --pmc: a few GEMV launches on both layers, then a plain "
+                         "device copy of COPY_BYTES (the counters' calibration), nothing else")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -243,6 +274,8 @@ def main() -> int:
     stream = torch.cuda.current_stream().cuda_stream
 
     layers = synth.WORKLOADS["opt175b_3bit"]
+    if args.counter_pass:
+        return counter_pass(lw, torch, layers, stream)
     footprint = sum(product_bytes(L.N, L.K, L.bits, L.group_size, 0) for L in layers)
     copies = copies_for(footprint)
     log(f"[bench] preparing {len(layers)} layers, {copies} weight copies "
@@ -261,27 +294,30 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronized on both sides
+    # timed region: exactly `steps` steps, synchronized on both sides; HIP events
+    # on the launch stream (torch's current stream) bracket the same region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
         step(args.warmup + i)
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes * args.steps / wall / 1e9
+    launches = len(preps)
+    avg_launch_ms = ev0.elapsed_time(ev1) / (args.steps * launches)
+    avg_bytes = step_bytes / launches
+    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
 
-    # per-launch device time of the same launches (HIP events on the launch stream)
+    # per-layer device time, each launch bracketed by its own events (context)
     per_layer = {}
-    total_ms = 0.0
     for j, p in enumerate(preps):
         avg, med = time_launches(torch, lambda i, p=p: run_product(lw, p, 1, i, stream, "qgemv"),
                                  args.steps)
         per_layer[p.layer.name] = (avg, med)
-        total_ms += avg
-    launches = len(preps)
-    avg_launch_ms = total_ms / launches
-    avg_bytes = step_bytes / launches
-    achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
     traffic = load_traffic(avg_bytes)
 
     result = {
