@@ -3,23 +3,32 @@
 //
 // y[b][n] = sum_k x[b][k] * deq(packed[n])[k] with deq = fp16_rne((q - z) * s),
 // the same contract as the matrix-vector kernel; this one is for batches
-// where the product is a real dense contraction (16 and more activation rows).
-// The weights are still decoded by the vector ALUs from their low-bit form
-// ([Feature Request] 4bit and 2bit and 1bit quantization support: 4-bit
-// weights kept on the GPU and converted by its cores at run time); the
-// decoded fp16 values go straight from registers into the MFMA B operand.
+// where the product is a real dense contraction (the matrix cores do the
+// multiply-adds, the vector ALUs only decode).  The weights are decoded from
+// their low-bit form by the GPU's own cores at run time ([Feature Request]
+// 4bit and 2bit and 1bit quantization support) and go from registers straight
+// into the MFMA B operand.
 //
-// Tiling (one workgroup = 4 waves = 64 weight rows x 16*BT batch rows):
-//  - MFMA 16x16x32: the 16 "columns" are 16 weight rows, the 16 "rows" are
-//    16 batch rows, the 32-long contraction is 4 lane groups x 8 fp16 each;
-//  - lane l of a wave decodes one unit (see unit_decode.h) of weight row
-//    (l % 16); lane group h = l / 16 takes unit h of the current K tile, so a
-//    K tile is 4 units (128 codes at 4 bits, 256 at 2 and 3 bits);
-//  - a unit's slots 4s..4s+3 (8 fp16 values) are the B operand of MFMA step s;
-//    the activation tile is staged in LDS in the same slot order (double
-//    buffered), so the A operand is one 16-byte LDS read per lane and step;
-//  - the contraction order inside the 32-long step is the slot order, which
-//    is a permutation of k applied identically to both operands.
+// Work layout (one persistent workgroup of 8 waves per CU):
+//  - the weight rows are cut into groups of 16 (the MFMA's 16 columns); each
+//    workgroup owns an equal, contiguous share of the groups and walks them
+//    in rounds of at most 8 groups;
+//  - in a round, wave w works on row group (w % RG) and K part (w / RG): with
+//    RG groups in the round, KP = 8 / RG waves split K between them, so few
+//    groups per CU still keep all waves busy;
+//  - K is walked in tiles; a tile holds, for every K part, four lane groups
+//    times NU consecutive units (see unit_decode.h) per row;  lane l decodes
+//    row (l % 16) of its group, lane group h = l / 16 takes its NU units, so
+//    the four lanes of a row read 4 * NU * 16 contiguous bytes;
+//  - x for the tile (all batch rows, zero past K and past B) is staged in
+//    LDS, double buffered, already in the decode's slot order, so one MFMA A
+//    operand is one 16-byte LDS read; the next tile's weights and x are
+//    loaded while the current tile is multiplied;
+//  - each wave keeps 16 x (16 * BT) fp32 accumulators in registers over all
+//    of K; at the end of a round the K parts meet in LDS and are summed in a
+//    fixed order (deterministic), and y is written with coalesced stores.
+//  - the contraction order inside one 32-long MFMA step is the slot order, a
+//    permutation of k applied identically to both operands.
 #include "common.h"
 #include "kernels.h"
 #include "unit_decode.h"
@@ -28,179 +37,420 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kWaves = 8;  // two per SIMD: each wave may hold 256 registers
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTileK = 512;  // k extent of one step: its activations are one LDS buffer
 
-template <int BITS>
-__device__ __forceinline__ UnitRef gemm_unit(int t, int h, int K) {
-  UnitRef u;
+typedef uint32_t u3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Group layout of the scales and zeros: one per row, power-of-two groups
+// (group index by a shift), or any other group size (a division).
+enum GroupMode { kPerRow = 0, kPow2Groups = 1, kAnyGroups = 2 };
+
+// Scales and zeros of constant set c of unit u: its low and high halves'
+// groups (a position past the row end takes the last group of the row, a
+// finite scale; its weight meets a zero activation).
+template <int BITS, int GM>
+__device__ __forceinline__ HalfParams params_at(const uint16_t* __restrict__ srow,
+                                                const int32_t* __restrict__ zrow, int gsz,
+                                                int gshift, const UnitRef& u, int c, int K) {
+  int kl, kh;
   if constexpr (BITS == 3) {
-    const int pa = 8 * t + h, pb = pa + 4;
-    u.ka = 32 * pa;
-    u.kb = 32 * pb;
-    u.va = u.ka < K;
-    u.vb = u.kb < K;
+    kl = u.ka;
+    kh = u.kb;
+  } else if constexpr (BITS == 2) {
+    kl = kh = u.ka + 32 * c;
   } else {
-    constexpr int C = Unit<BITS>::CODES;
-    u.ka = C * (4 * t + h);
-    u.kb = u.ka;
-    u.va = u.ka < K;
-    u.vb = u.va;
+    kl = kh = u.ka;
   }
-  return u;
+  const uint32_t cl = (uint32_t)min(kl, K - 1), ch = (uint32_t)min(kh, K - 1);
+  const uint32_t gl = GM == kPow2Groups ? cl >> gshift : cl / (uint32_t)gsz;
+  const uint32_t gh = GM == kPow2Groups ? ch >> gshift : ch / (uint32_t)gsz;
+  HalfParams hp;
+  hp.s_lo = srow[gl];
+  hp.s_hi = srow[gh];
+  hp.z_lo = zrow[gl];
+  hp.z_hi = zrow[gh];
+  hp.v_lo = kl < K;
+  hp.v_hi = kh < K;
+  return hp;
 }
 
-template <int BITS>
-constexpr int codes_per_tile() {
-  return 4 * Unit<BITS>::CODES;
-}
-
-template <int BITS, int BT, bool PERROW>
-__global__ __launch_bounds__(kGemmThreads) void qgemm_kernel(
+template <int BITS, int BT, int GM>
+__global__ __launch_bounds__(kThreads) void qgemm_kernel(
     const uint16_t* __restrict__ x, int B, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
-    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift, int T) {
+    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift) {
   using U = Unit<BITS>;
-  constexpr int S = U::QUADS;  // MFMA steps per unit
-  // [buffer][bt][s][h][i]: 16-byte A operands, lane (i, h) reads consecutive entries
-  __shared__ uint4 xs[2][BT][S][4][16];
+  constexpr int Q = U::QUADS, W = U::WORDS, NC = U::NCONST;
+  constexpr bool PERROW = GM == kPerRow;
+  constexpr int BP = 16 * BT;               // batch rows per pass (padded)
+  constexpr int UT = kTileK / U::CODES;     // units (3-bit: period pairs) per step
+  constexpr int NWMAX = UT / 4;             // units per lane and step (one K part)
+  constexpr int E = 2 * BT;                 // activation entries per thread and step
+  constexpr int XBUF = kTileK * BP * 2 / 16;  // 16-byte entries of one activation buffer
+  static_assert(XBUF == E * kThreads, "one step's activations are E entries per thread");
+  // LDS: two activation tiles (later the partial sums), then per-wave scratch
+  // of the exact decode path
+  extern __shared__ uint4 lds[];
+  uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(lds + 2 * XBUF);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, h = lane >> 4;
-  const int n = blockIdx.x * (kGemmWaves * 16) + wave * 16 + i16;
-  const bool nv = n < N;
-  const int nn = nv ? n : N - 1;
-  const int b0 = blockIdx.y * 16 * BT;
-  const int64_t wpr = (int64_t)K * BITS / 32;
-  const uint32_t* rowp = packed + (int64_t)nn * wpr;
-  const uint16_t* srow = scales + (int64_t)nn * G;
-  const int32_t* zrow = zeros + (int64_t)nn * G;
+  const uint32_t row_bytes = (uint32_t)K * BITS / 8;
+  const int row_words = (int)(row_bytes / 4);
+  const int units_per_row = BITS == 3 ? K / 32 : (K + U::CODES - 1) / U::CODES;  // 3-bit: periods
+  const auto xrs = make_rsrc(x, (uint32_t)((int64_t)B * K * 2));
 
-  auto stage = [&](int t, int buf) {
-    // BT*S*4*16 entries, 256 threads
-    for (int e = tid; e < BT * S * 64; e += kGemmThreads) {
-      const int ei = e & 15, eh = (e >> 4) & 3;
-      const int rest = e >> 6;
-      const int es = rest % S, ebt = rest / S;
-      const int b = b0 + 16 * ebt + ei;
-      const UnitRef u = gemm_unit<BITS>(t, eh, K);
-      const bool bv = b < B;
-      xs[buf][ebt][es][eh][ei] = x_entry<BITS>(x + (int64_t)(bv ? b : 0) * K, u, es, bv);
-    }
-  };
-
-  HalfParams rowp_;
-  Consts<BITS> rowc[U::NCONST];
-  bool rowfast = true;
-  if constexpr (PERROW) {
-    rowp_.s_lo = rowp_.s_hi = srow[0];
-    rowp_.z_lo = rowp_.z_hi = zrow[0];
-    rowp_.v_lo = rowp_.v_hi = true;
-#pragma unroll
-    for (int c = 0; c < U::NCONST; ++c) rowfast &= make_consts<BITS, false>(rowp_, rowc[c]);
-  }
+  const int NG = (N + 15) / 16;
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int gb = NG / nwg, ge = NG % nwg;
+  const int g0 = wg * gb + min(wg, ge);
+  const int g1 = g0 + gb + (wg < ge ? 1 : 0);
 
   const uint32_t mg = magic_register();
-  f4_t acc[BT];
-#pragma unroll
-  for (int bt = 0; bt < BT; ++bt) acc[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  stage(0, 0);
-  __syncthreads();
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T) stage(t + 1, buf ^ 1);
+  for (int gr0 = g0; gr0 < g1; gr0 += kWaves) {
+    const int RG = min(kWaves, g1 - gr0);
+    // K parts: the largest power of two that fits both the waves and the step
+    int KP = 1;
+    while (KP * 2 * RG <= kWaves && KP * 2 <= NWMAX) KP *= 2;
+    const int NW = NWMAX / KP;  // units per lane and step
+    const int T = BITS == 3 ? (units_per_row + 2 * UT - 1) / (2 * UT)
+                            : (units_per_row + UT - 1) / UT;
+    const bool active = wave < RG * KP;
+    const int gl = wave % RG, kp = wave / RG;
+    const int grp = gr0 + gl;
+    const int n = min(16 * grp + i16, N - 1);
+    const int rows_here = max(0, min(16, N - 16 * grp));
+    // buffer descriptor over this wave's 16 rows (rows past N read zeros);
+    // its parts are made explicitly wave-uniform, or the compiler would keep
+    // it in vector registers and loop over its distinct values at every load
+    const uint64_t rbase = reinterpret_cast<uint64_t>(packed + (int64_t)16 * min(grp, NG - 1) * row_words);
+    const uint32_t rlo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)rbase);
+    const uint32_t rhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(rbase >> 32));
+    const uint32_t rbytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)min((int64_t)rows_here * row_bytes, (int64_t)0x7fffffff));
+    const auto rs = make_rsrc(reinterpret_cast<const void*>(((uint64_t)rhi << 32) | rlo), rbytes);
+    const uint32_t row_off = (uint32_t)i16 * row_bytes;
+    const uint16_t* srow = scales + (int64_t)n * G;
+    const int32_t* zrow = zeros + (int64_t)n * G;
 
-    const UnitRef u = gemm_unit<BITS>(t, h, K);
-    uint32_t w[U::WORDS];
-    load_unit<BITS>(rowp, u, w);
-    HalfParams hp[U::NCONST];
-    Consts<BITS> cc[U::NCONST];
-    bool fast = true;
-    const bool full = u.va && u.vb;
+    // per-row constants (one group per row): computed once per round
+    Consts<BITS> rowc;
+    bool rowfast = true;
+    HalfParams rowp{};
     if constexpr (PERROW) {
+      rowp = HalfParams{srow[0], srow[0], zrow[0], zrow[0], true, true};
+      rowfast = make_consts<BITS, false>(rowp, rowc);
+      // positions past the end of the row decode garbage words against zero
+      // activations: only a finite decode is needed there (|q - z| * s < 65504)
+      rowfast &= rowp.s_lo < 0x6C00u;
+    }
+
+    f4_t acc[BT];
 #pragma unroll
-      for (int c = 0; c < U::NCONST; ++c) {
-        hp[c] = rowp_;
-        if (full) {
-          cc[c] = rowc[c];
+    for (int bt = 0; bt < BT; ++bt) acc[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // unit ug of step t (4-bit / 2-bit: CODES codes; 3-bit: two periods)
+    auto unit_at = [&](int t, int ug) {
+      UnitRef u;
+      if constexpr (BITS == 3) {
+        const int pa = 2 * UT * t + ug, pb = pa + UT;
+        u.ka = 32 * pa;
+        u.kb = 32 * pb;
+      } else {
+        u.ka = U::CODES * (UT * t + ug);
+        u.kb = u.ka;
+      }
+      u.va = u.ka < K;
+      u.vb = u.kb < K;
+      return u;
+    };
+    // the four lanes of a row (lane groups h) read 4 * NW consecutive units
+    auto my_unit = [&](int t, int u) { return unit_at(t, (kp * 4 + h) * NW + u); };
+
+    struct WBuf {
+      uint32_t w[NWMAX][W];
+      HalfParams hp[PERROW ? 1 : NWMAX][NC];  // grouped layouts: the units' scales and zeros
+    };
+    // Weight loads of step t: always NWMAX units per lane (clamped to the row,
+    // unused ones discarded), so every step issues the same number of loads.
+    auto load_w = [&](int t, WBuf& b) {
+#pragma unroll
+      for (int u = 0; u < NWMAX; ++u) {
+        const UnitRef ur = my_unit(t, u < NW ? u : 0);
+        if constexpr (BITS == 3) {
+          const int pa = min(ur.ka >> 5, units_per_row - 1), pb = min(ur.kb >> 5, units_per_row - 1);
+          const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, row_off + 12u * pa, 0, 2);
+          const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, row_off + 12u * pb, 0, 2);
+          b.w[u][0] = va.x;
+          b.w[u][1] = va.y;
+          b.w[u][2] = va.z;
+          b.w[u][3] = vb.x;
+          b.w[u][4] = vb.y;
+          b.w[u][5] = vb.z;
         } else {
-          hp[c].v_lo = u.va;
-          hp[c].v_hi = u.vb;
-          fast &= make_consts<BITS, false>(hp[c], cc[c]);
+          const int gu = min(ur.ka >> (BITS == 4 ? 5 : 6), units_per_row - 1);
+          const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + 16u * gu, 0, 2);
+          b.w[u][0] = v.x;
+          b.w[u][1] = v.y;
+          b.w[u][2] = v.z;
+          b.w[u][3] = v.w;
+        }
+        // grouped layouts: this unit's scales and zeros come with its words
+        // (positions past the row end take the row's last group)
+        if constexpr (!PERROW) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
         }
       }
-      if (full) fast = rowfast;
-    } else {
+    };
+
+    // Activation staging of step t: every thread stages E entries (all batch
+    // rows of one 512-k step), issuing the same loads every step; halves past
+    // K or past B read zeros (their offset lies outside the buffer
+    // descriptor).  One wave instruction covers the 64 (unit, quad) entries of
+    // one batch row, so its loads read that row's x contiguously; 4-bit
+    // entries are eight consecutive k (one 16-byte load), 2- and 3-bit
+    // entries two runs of four (two 8-byte loads).  In LDS, entry (m = unit
+    // slot * Q + quad, batch tile, lane group h, batch row i16) sits at
+    // (m * BT + bt) * 64 + 16 h + (i16 ^ (m & 15)): the swizzle spreads one
+    // wave's scattered writes over all banks, and the MFMA operand reads stay
+    // one contiguous block per 16 lanes.  Offsets are worked out once per
+    // round; a step only advances them by the step's K extent.
+    static_assert(UT * Q == 64, "one wave instruction stages one batch row of a step");
+    int xk[E][2];           // first k of each half at step 0 (K: never valid)
+    uint32_t xo[E][2];      // byte offset of that k in x
+    int xl[E];              // LDS entry of the thread's entry
 #pragma unroll
-      for (int c = 0; c < U::NCONST; ++c) {
-        hp[c] = load_params<BITS>(srow, zrow, gsz, gshift, u, c);
-        fast &= make_consts<BITS, false>(hp[c], cc[c]);
+    for (int i = 0; i < E; ++i) {
+      const int e = tid + i * kThreads;
+      const int ml = e & 63, b = e >> 6;
+      const int ul = ml / Q, q = ml % Q;      // unit of the step, quad
+      const int eh = (ul / NW) & 3, ekp = ul / (4 * NW), eu = ul % NW;
+      const UnitRef ur = unit_at(0, ul);
+      const int kl = unit_k<BITS>(ur, U::lo(4 * q)), kh = unit_k<BITS>(ur, U::hi(4 * q));
+      xk[i][0] = b < B ? kl : K;
+      xk[i][1] = b < B ? kh : K;
+      xo[i][0] = 2u * ((uint32_t)b * (uint32_t)K + (uint32_t)kl);
+      xo[i][1] = 2u * ((uint32_t)b * (uint32_t)K + (uint32_t)kh);
+      const int m = (ekp * NW + eu) * Q + q;
+      xl[i] = (m * BT + (b >> 4)) * 64 + 16 * eh + ((b & 15) ^ (m & 15));
+    }
+    uint4 xr[E];
+    auto fetch_x = [&](int t) {
+      const int tk = t * kTileK;
+      const uint32_t tb = 2u * (uint32_t)tk;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const uint32_t ol = xk[i][0] + tk < K ? xo[i][0] + tb : 0xFFFFFFF0u;
+        if constexpr (BITS == 4) {
+          const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, ol, 0, 0);
+          xr[i] = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+          const uint32_t oh = xk[i][1] + tk < K ? xo[i][1] + tb : 0xFFFFFFF0u;
+          const auto la = __builtin_amdgcn_raw_buffer_load_b64(xrs, ol, 0, 0);
+          const auto lb = __builtin_amdgcn_raw_buffer_load_b64(xrs, oh, 0, 0);
+          xr[i] = make_uint4(la[0], la[1], lb[0], lb[1]);
+        }
       }
+    };
+    auto store_x = [&](int buf) {
+      uint4* xs = lds + buf * XBUF;
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        xs[xl[i]] = make_uint4(__builtin_amdgcn_perm(xr[i].z, xr[i].x, 0x05040100u),
+                               __builtin_amdgcn_perm(xr[i].z, xr[i].x, 0x07060302u),
+                               __builtin_amdgcn_perm(xr[i].w, xr[i].y, 0x05040100u),
+                               __builtin_amdgcn_perm(xr[i].w, xr[i].y, 0x07060302u));
+    };
+
+    auto compute = [&](int t, int buf, WBuf& b) {
+      if (!active) return;
+      const uint4* xs = lds + buf * XBUF;
+#pragma unroll
+      for (int u = 0; u < NWMAX; ++u) {
+        if (u < NW) {
+          const UnitRef ur = my_unit(t, u);
+          HalfParams hp[NC];
+          Consts<BITS> cc[NC];
+          bool fast;
+          if constexpr (PERROW) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              hp[c] = rowp;
+              hp[c].v_lo = ur.va;
+              hp[c].v_hi = ur.vb;
+              cc[c] = rowc;
+            }
+            fast = rowfast;
+          } else {
+            fast = true;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              hp[c] = b.hp[u][c];
+              fast &= make_consts<BITS, false>(hp[c], cc[c]);
+            }
+          }
+          // entries of (kp, u) for this lane: [s][bt] blocks of 64, swizzled
+          const int m0 = (kp * NW + u) * Q;
+          const uint4* xe = xs + (m0 * BT) * 64 + h * 16;
+          if (__all(fast)) {
+#pragma unroll
+            for (int s = 0; s < Q; ++s) {
+              const h8_t bv = __builtin_bit_cast(
+                  h8_t, make_uint4(as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 0,
+                                                                 cc[U::cset(4 * s + 0)], mg)),
+                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 1,
+                                                                 cc[U::cset(4 * s + 1)], mg)),
+                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 2,
+                                                                 cc[U::cset(4 * s + 2)], mg)),
+                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 3,
+                                                                 cc[U::cset(4 * s + 3)], mg))));
+#pragma unroll
+              for (int bt = 0; bt < BT; ++bt) {
+                const h8_t av = __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
+                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
+              }
+            }
+          } else {
+            // exact per-code path (tiny or subnormal scales, zero points far
+            // from the grid, huge scales); one quad per loop trip, the unit's
+            // words read back from this wave's LDS scratch
+            uint32_t* wsc = slow_scratch + wave * (W * 64);
+#pragma unroll
+            for (int i = 0; i < W; ++i) wsc[i * 64 + lane] = b.w[u][i];
+#pragma unroll 1
+            for (int s = 0; s < Q; ++s) {
+              h2_t d[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int slot = 4 * s + e;
+                const HalfParams hh = (NC == 1 || U::cset(slot) == 0) ? hp[0] : hp[NC - 1];
+                const int ql = (int)unit_code_lds<BITS>(wsc, lane, U::lo(slot));
+                const int qh = (int)unit_code_lds<BITS>(wsc, lane, U::hi(slot));
+                const uint16_t dl =
+                    hh.v_lo ? exact_deq(ql, hh.z_lo, h_bits_to_f32(hh.s_lo)) : (uint16_t)0;
+                const uint16_t dh =
+                    hh.v_hi ? exact_deq(qh, hh.z_hi, h_bits_to_f32(hh.s_hi)) : (uint16_t)0;
+                d[e] = as_h2((uint32_t)dl | ((uint32_t)dh << 16));
+              }
+              const h8_t bv = __builtin_bit_cast(
+                  h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
+#pragma unroll
+              for (int bt = 0; bt < BT; ++bt) {
+                const h8_t av = __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
+                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+    };
+
+    // One step per activation tile.  Step t: fetch x of step t+1, load the
+    // weights of step t+1, multiply step t, store x of step t+1, barrier.  The
+    // loads past the last step are clamped and their data unused; issuing
+    // them anyway keeps every wait exact (the decode waits only for its own
+    // weights, the store only for the activations).
+    WBuf wa, wb;
+    fetch_x(0);
+    load_w(0, wa);
+    store_x(0);
+    __syncthreads();
+    for (int t = 0; t < T; t += 2) {
+      fetch_x(min(t + 1, T - 1));
+      load_w(min(t + 1, T - 1), wb);
+      compute(t, 0, wa);
+      if (t + 1 < T) store_x(1);
+      __syncthreads();
+      if (t + 1 >= T) break;
+      fetch_x(min(t + 2, T - 1));
+      load_w(min(t + 2, T - 1), wa);
+      compute(t + 1, 1, wb);
+      if (t + 2 < T) store_x(0);
+      __syncthreads();
     }
 
-    h2_t bop[S][4];
-    if (__all(fast)) {
+    // K parts meet in LDS: red[(gl * KP + kp)][b][j], b < BP, j < 16
+    float* red = reinterpret_cast<float*>(lds);
+    if (active) {
 #pragma unroll
-      for (int s = 0; s < S; ++s)
+      for (int bt = 0; bt < BT; ++bt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bop[s][e] = fast_pair<BITS, false>(w, 4 * s + e, cc[U::cset(4 * s + e)], mg);
-    } else {
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bop[s][e] = slow_pair<BITS>(w, 4 * s + e, hp[U::cset(4 * s + e)]);
-    }
-
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const h8_t bv = __builtin_bit_cast(
-          h8_t, make_uint4(as_u32(bop[s][0]), as_u32(bop[s][1]), as_u32(bop[s][2]),
-                           as_u32(bop[s][3])));
-#pragma unroll
-      for (int bt = 0; bt < BT; ++bt) {
-        const h8_t av = __builtin_bit_cast(h8_t, xs[buf][bt][s][h][i16]);
-        acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int b = 16 * bt + 4 * h + r;
+          red[((gl * KP + kp) * BP + b) * 16 + i16] = acc[bt][r];
+        }
     }
     __syncthreads();
-  }
-
-  // D layout: lane l holds rows 4*(l/16) + r (batch) of column l%16 (weight row)
-  if (nv) {
-#pragma unroll
-    for (int bt = 0; bt < BT; ++bt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int b = b0 + 16 * bt + 4 * h + r;
-        if (b < B) y[(int64_t)b * N + n] = f32_to_h_bits(acc[bt][r]);
-      }
+    const int outs = RG * 16 * B;
+    for (int e = tid; e < outs; e += kThreads) {
+      const int j = e & 15;
+      const int rest = e >> 4;
+      const int g = rest % RG, b = rest / RG;
+      const int row = 16 * (gr0 + g) + j;
+      float v = 0.0f;
+      for (int p = 0; p < KP; ++p) v += red[((g * KP + p) * BP + b) * 16 + j];
+      if (row < N) y[(int64_t)b * N + row] = f32_to_h_bits(v);
+    }
+    __syncthreads();  // the LDS is reused by the next round
   }
 }
 
-template <int BITS, int BT, bool PERROW>
+template <int BITS, int BT, int GM>
 hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
-  const int T = (K + codes_per_tile<BITS>() - 1) / codes_per_tile<BITS>();
-  const dim3 grid((unsigned)((N + kGemmWaves * 16 - 1) / (kGemmWaves * 16)),
-                  (unsigned)((B + 16 * BT - 1) / (16 * BT)));
-  hipLaunchKernelGGL((qgemm_kernel<BITS, BT, PERROW>), grid, dim3(kGemmThreads), 0, stream, x, B,
-                     packed, scales, zeros, y, N, K, G, gsz, gshift, T);
+  const size_t lds = 2 * (size_t)kTileK * 16 * BT * 2 + (size_t)kWaves * Unit<BITS>::WORDS * 64 * 4;
+  if (lds > device_lds_per_block()) return hipErrorNotSupported;
+  const auto kern = qgemm_kernel<BITS, BT, GM>;
+  // the LDS request exceeds the default limit: raise it once per device
+  static int raised[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!raised[dev]) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised[dev] = 1;
+  }
+  const int NG = (N + 15) / 16;
+  const int cus = device_cu_count();
+  const int grid = NG < cus ? NG : cus;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, x, B, packed, scales, zeros,
+                     y, N, K, G, gsz, gshift);
   return hipGetLastError();
 }
 
-template <int BITS, bool PERROW>
+template <int BITS, int GM>
 hipError_t launch_bits(int B, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                        const int32_t* zeros, int N, int K, int G, int gsz, int gshift,
                        uint16_t* y, hipStream_t stream) {
-  if (B <= 16)
-    return launch_t<BITS, 1, PERROW>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, y, stream);
-  if (B <= 32)
-    return launch_t<BITS, 2, PERROW>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, y, stream);
-  return launch_t<BITS, 4, PERROW>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, y, stream);
+  // batches beyond 64 rows run as several passes over the weights
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bc = B - b0 < 64 ? B - b0 : 64;
+    const uint16_t* xb = x + (int64_t)b0 * K;
+    uint16_t* yb = y + (int64_t)b0 * N;
+    hipError_t e;
+    if (bc <= 16)
+      e = launch_t<BITS, 1, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+    else if (bc <= 32)
+      e = launch_t<BITS, 2, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+    else
+      e = launch_t<BITS, 4, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -211,19 +461,29 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
-  const bool perrow = G == 1;
+  const int gm = G == 1 ? kPerRow : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
+#define LOWBIT_QGEMM_GM(bits_)                                                                  \
+  switch (gm) {                                                                                 \
+    case kPerRow:                                                                               \
+      return launch_bits<bits_, kPerRow>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y,   \
+                                         stream);                                               \
+    case kPow2Groups:                                                                           \
+      return launch_bits<bits_, kPow2Groups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift,  \
+                                             y, stream);                                        \
+    default:                                                                                    \
+      return launch_bits<bits_, kAnyGroups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, \
+                                            stream);                                            \
+  }
   switch (bits) {
     case 2:
-      return perrow ? launch_bits<2, true>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream)
-                    : launch_bits<2, false>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      LOWBIT_QGEMM_GM(2)
     case 3:
-      return perrow ? launch_bits<3, true>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream)
-                    : launch_bits<3, false>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      LOWBIT_QGEMM_GM(3)
     default:
-      return perrow ? launch_bits<4, true>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream)
-                    : launch_bits<4, false>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      LOWBIT_QGEMM_GM(4)
   }
+#undef LOWBIT_QGEMM_GM
 }
 
 }  // namespace lowbit
