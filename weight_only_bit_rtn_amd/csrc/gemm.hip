@@ -50,8 +50,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // Group layout of the scales and zeros: one per row, power-of-two groups
-// (group index by a shift), or any other group size (a division).
-enum GroupMode { kPerRow = 0, kPow2Groups = 1, kAnyGroups = 2 };
+// (group index by a shift), any other group size (a division), or
+// power-of-two groups at least as long as one lane's units of a step (2- and
+// 4-bit): then those units share one group, loaded once per step.
+enum GroupMode { kPerRow = 0, kPow2Groups = 1, kAnyGroups = 2, kWideGroups = 3 };
 
 // Scales and zeros of constant set c of unit u: its low and high halves'
 // groups (a position past the row end takes the last group of the row, a
@@ -70,8 +72,8 @@ __device__ __forceinline__ HalfParams params_at(const uint16_t* __restrict__ sro
     kl = kh = u.ka;
   }
   const uint32_t cl = (uint32_t)min(kl, K - 1), ch = (uint32_t)min(kh, K - 1);
-  const uint32_t gl = GM == kPow2Groups ? cl >> gshift : cl / (uint32_t)gsz;
-  const uint32_t gh = GM == kPow2Groups ? ch >> gshift : ch / (uint32_t)gsz;
+  const uint32_t gl = GM == kAnyGroups ? cl / (uint32_t)gsz : cl >> gshift;
+  const uint32_t gh = GM == kAnyGroups ? ch / (uint32_t)gsz : ch >> gshift;
   HalfParams hp;
   hp.s_lo = srow[gl];
   hp.s_hi = srow[gh];
@@ -179,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
 
     struct WBuf {
       uint32_t w[NWMAX][W];
-      HalfParams hp[PERROW ? 1 : NWMAX][NC];  // grouped layouts: the units' scales and zeros
+      // grouped layouts: the units' scales and zeros (one set per step when
+      // the lane's units share a group)
+      HalfParams hp[PERROW || GM == kWideGroups ? 1 : NWMAX][NC];
     };
     // Weight loads of step t: always NWMAX units per lane (clamped to the row,
     // unused ones discarded), so every step issues the same number of loads.
@@ -207,10 +211,16 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
         }
         // grouped layouts: this unit's scales and zeros come with its words
         // (positions past the row end take the row's last group)
-        if constexpr (!PERROW) {
+        if constexpr (GM == kPow2Groups || GM == kAnyGroups) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
+        } else if constexpr (GM == kWideGroups) {
+          if (u == 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              b.hp[0][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
+          }
         }
       }
     };
@@ -297,7 +307,11 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
             fast = true;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-              hp[c] = b.hp[u][c];
+              hp[c] = b.hp[GM == kWideGroups ? 0 : u][c];
+              if constexpr (GM == kWideGroups) {  // the shared group; this unit's validity
+                hp[c].v_lo = ur.va;
+                hp[c].v_hi = ur.vb;
+              }
               fast &= make_consts<BITS, false>(hp[c], cc[c]);
             }
           }
@@ -461,7 +475,10 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
-  const int gm = G == 1 ? kPerRow : gshift >= 0 ? kPow2Groups : kAnyGroups;
+  // wide groups: a lane's units of one step (at most 4 x 32 codes at 4 bits,
+  // 2 x 64 at 2 bits, starting on a multiple of that span) lie in one group
+  const bool wide = bits != 3 && gshift >= 0 && gsz >= 128;
+  const int gm = G == 1 ? kPerRow : wide ? kWideGroups : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
 #define LOWBIT_QGEMM_GM(bits_)                                                                  \
   switch (gm) {                                                                                 \
@@ -471,6 +488,9 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
     case kPow2Groups:                                                                           \
       return launch_bits<bits_, kPow2Groups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift,  \
                                              y, stream);                                        \
+    case kWideGroups:                                                                           \
+      return launch_bits<bits_, (bits_ == 3 ? kPow2Groups : kWideGroups)>(                       \
+          b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);                        \
     default:                                                                                    \
       return launch_bits<bits_, kAnyGroups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, \
                                             stream);                                            \
