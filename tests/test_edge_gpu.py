@@ -6,6 +6,7 @@ slow decode), round-half-to-even ties, empty problems and error returns."""
 from __future__ import annotations
 
 import ctypes
+import sys
 
 import numpy as np
 import pytest
@@ -30,6 +31,11 @@ def _to_gpu(a):
     if a.dtype == np.uint32:
         a = a.view(np.int32)
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
 
 
 def _sync():
@@ -90,6 +96,88 @@ def _quant_cases():
 @pytest.mark.parametrize("kind", ["normal", "mixed"])
 def test_quantize_shapes(lw, bits, N, K, g, kind):
     w = _weights(kind, N, K, seed=N * 131 + K + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    out = lw.quantize_rtn(_to_gpu(w), bits, g)
+    _sync()
+    assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16), scales.view(np.uint16))
+    assert np.array_equal(out["zeros"].cpu().numpy(), zeros)
+    assert np.array_equal(out["codes"].cpu().numpy(), codes)
+    assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), packed)
+
+
+# Group sizes and row lengths that reach every reduction layout of the
+# quantizer: groups of 32 and 64 lanes, power-of-two groups larger than a
+# wave, groups that are not a power of two, rows of 1024 threads with up to
+# 16 chunks per thread (the largest row), and ragged last rounds.
+GROUP_PATH_CASES = [
+    (4, 6, 4096, 256),
+    (2, 6, 4096, 512),
+    (3, 5, 8192, 1024),
+    (4, 4, 8192, 2048),
+    (4, 7, 12320, 160),
+    (3, 2, 98304, 96),
+    (2, 3, 65600, 0),
+    (2, 3, 131072, 0),
+    (3, 2, 131072, 64),
+    (4, 2, 131072, 16384),
+]
+
+
+@pytest.mark.parametrize("bits,N,K,g", GROUP_PATH_CASES)
+@pytest.mark.parametrize("kind", ["normal", "mixed"])
+def test_quantize_group_paths(lw, bits, N, K, g, kind):
+    _say(f"[quantize paths] bits={bits} N={N} K={K} g={g} {kind}")
+    w = _weights(kind, N, K, seed=K + g + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    for want_codes in (True, False):
+        out = lw.quantize_rtn(_to_gpu(w), bits, g, codes=want_codes, packed=True)
+        _sync()
+        assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16), scales.view(np.uint16))
+        assert np.array_equal(out["zeros"].cpu().numpy(), zeros)
+        if want_codes:
+            assert np.array_equal(out["codes"].cpu().numpy(), codes)
+        assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), packed)
+
+
+def _scale_tie_groups(bits: int, count: int) -> list:
+    """(lo, hi) fp16 pairs whose fp32 quotient (hi - lo) / M lies exactly
+    half-way between two fp16 values, so the stored scale depends on the
+    quotient being rounded to fp32 before fp16 (ties to even)."""
+    M = np.float32((1 << bits) - 1)
+    found = []
+    for lo in (np.float16(-0.5), np.float16(-1.0), np.float16(0.25)):
+        his = np.arange(0x2000, 0x3C00, dtype=np.uint16).view(np.float16)
+        his = his[his.astype(np.float32) > np.float32(lo)]
+        d = his.astype(np.float32) - np.float32(lo)
+        s32 = (d / M).astype(np.float32)
+        s16 = s32.astype(np.float16)
+        down = np.nextafter(s16, np.float16(-np.inf))
+        up = np.nextafter(s16, np.float16(np.inf))
+        half_dn = (s16.astype(np.float64) + down.astype(np.float64)) / 2
+        half_up = (s16.astype(np.float64) + up.astype(np.float64)) / 2
+        tie = (s32.astype(np.float64) == half_dn) | (s32.astype(np.float64) == half_up)
+        found += [(lo, h) for h in his[tie][:count]]
+    assert found, "no halfway scale found"
+    return found[: count]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("g", [0, 32, 96])
+def test_quantize_scale_ties(lw, bits, g):
+    """Regression: the scale is rounded to fp32, then to fp16, never once."""
+    _say(f"[quantize scale ties] bits={bits} g={g}")
+    pairs = _scale_tie_groups(bits, 12)
+    gs = g if g else 384
+    rng = np.random.default_rng(bits * 7 + g)
+    rows = []
+    for lo, hi in pairs:
+        grp = rng.uniform(float(lo), float(hi), gs).astype(np.float16)
+        grp[rng.integers(0, gs)] = lo
+        grp[rng.integers(0, gs)] = hi
+        grp = np.clip(grp, lo, hi)
+        reps = 384 // gs
+        rows.append(np.tile(grp, reps))
+    w = np.stack(rows).astype(np.float16)
     codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
     out = lw.quantize_rtn(_to_gpu(w), bits, g)
     _sync()

@@ -9,10 +9,28 @@
 // int32); the bit order (least significant first, 3-bit codes straddling
 // words) is this library's choice.
 //
-// Both kernels are HBM-streaming passes; one thread owns whole 32-code
-// "periods" (64 bytes of fp16 weights, BITS words of packed codes), so every
-// period packs into whole 32-bit words and every lane's loads and stores are
-// contiguous with its neighbours'.
+// Layout of the work: a lane owns "chunks" of 8 consecutive weights (16 bytes
+// of fp16, one 128-bit load).  Chunk c of a row is handled by thread c mod T
+// of the row's workgroup, so every load and store instruction of a wave
+// covers one contiguous span.  A chunk's 8 codes pack into 32 bits (4-bit),
+// 16 bits (2-bit) or 24 bits (3-bit; four neighbouring lanes then assemble
+// the three 32-bit words of their 32 codes with a DPP lane exchange).  The
+// whole row stays in registers between the min/max pass and the code pass, so
+// every weight is read from memory once.
+//
+// Arithmetic.  The codes need fl32(w / s) exactly (one IEEE division per
+// weight).  With r_hi = fl32(1/s) and r_lo = fl32(fma(-s, r_hi, 1) * r_hi),
+// r_hi + r_lo equals 1/s to about 2^-47 relative, and
+//     fl32(w / s) == fma(w, r_hi, fl32(w * r_lo))
+// for every pair of fp16 values w and s > 0: the quotient of two 11-bit
+// significands is never within 2^-36 (relative) of an fp32 rounding midpoint,
+// while the right-hand side is within 2^-45 of w / s before its single
+// rounding.  The identity was checked exhaustively over all fp16 w and all
+// positive finite fp16 s, and for d / M (fp32 d, M = 3, 7, 15) over every fp32
+// significand.  Rounding to an integer uses v + 1.5 * 2^23, whose fp32 sum
+// rounds v half-to-even onto the integer grid; the codes' quotients are
+// bounded by 2^16 in magnitude (the largest |w| / s of any group of finite
+// fp16 values), far inside the 2^22 range where that is exact.
 #include "common.h"
 #include "kernels.h"
 
@@ -22,231 +40,444 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kQuantThreads = 256;
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
-template <int BITS>
-__device__ __forceinline__ void pack_period(const uint32_t (&q)[32], uint32_t (&wd)[BITS]) {
-#pragma unroll
-  for (int i = 0; i < BITS; ++i) wd[i] = 0u;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    const int bit = BITS * c;
-    const int wi = bit >> 5;
-    const int off = bit & 31;
-    wd[wi] |= q[c] << off;
-    if (off + BITS > 32) wd[wi + 1] |= q[c] >> (32 - off);
-  }
+constexpr int kBufferDword3 = 0x00020000;      // raw 32-bit buffer format (gfx9 family)
+constexpr int kSlc = 2;                        // weights are streamed: read once
+constexpr float kRoundMagic = 12582912.0f;     // 1.5 * 2^23
+constexpr uint32_t kRoundBits = 0x4B400000u;   // its bit pattern
+constexpr uint32_t kPosInfPair = 0x7C007C00u;  // (+inf, +inf) as two fp16
+
+// How a row's groups are reduced.
+enum GroupMode {
+  kRowGroup = 0,    // one group per row: wave reductions, one barrier
+  kLaneGroups = 1,  // power-of-two groups of 4..64 chunks: lane butterflies, no LDS
+  kLdsGroups = 2,   // any other group size: chunk extrema through LDS, a wave per group
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferDword3);
 }
 
-template <int BITS>
-__device__ __forceinline__ void store_packed(uint32_t* dst, const uint32_t (&wd)[BITS]) {
-  if constexpr (BITS == 4) {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  } else if constexpr (BITS == 2) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
-  } else {
-    dst[0] = wd[0];
-    dst[1] = wd[1];
-    dst[2] = wd[2];
-  }
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_min(as_h2(a), as_h2(b)));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_max(as_h2(a), as_h2(b)));
+}
+// The same on raw loaded weights.  The builtins above first quiet possible
+// signalling NaNs of operands loaded from memory (one extra instruction per
+// operand); the weights are finite, so that step is skipped here.  The
+// results only feed ordinary instructions (never a DPP or lane read directly).
+__device__ __forceinline__ uint32_t pk_min_raw(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_raw(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
 
-__device__ __forceinline__ void load_period_f32(const uint16_t* src, float (&v)[32]) {
-  const uint4* p = reinterpret_cast<const uint4*>(src);
+// (min, -max) of a chunk's 8 fp16 values as an fp16 pair: taking -max lets
+// one packed minimum reduce both extrema.  Comparisons of fp16 values are
+// exact, so these are the very values an fp32 comparison would select.
+__device__ __forceinline__ uint32_t chunk_extrema(const u4_t& d) {
+  const uint32_t lo = pk_min_raw(pk_min_raw(d[0], d[1]), pk_min_raw(d[2], d[3]));
+  const uint32_t hi = pk_max_raw(pk_max_raw(d[0], d[1]), pk_max_raw(d[2], d[3]));
+  const h2_t l = as_h2(lo), h = as_h2(hi);
+  h2_t r;
+  r.x = __builtin_elementwise_min(l.x, l.y);
+  r.y = -__builtin_elementwise_max(h.x, h.y);
+  return as_u32(r);
+}
+
+// Reduce (min, -max) pairs over aligned groups of 4, 8 or 16 lanes.
+__device__ __forceinline__ uint32_t reduce_lanes16(uint32_t p, int lanes) {
+  p = pk_min(p, dpp<0xb1>(p));                  // quad_perm [1,0,3,2]
+  p = pk_min(p, dpp<0x4e>(p));                  // quad_perm [2,3,0,1]
+  if (lanes >= 8) p = pk_min(p, dpp<0x141>(p));   // row_half_mirror
+  if (lanes >= 16) p = pk_min(p, dpp<0x140>(p));  // row_mirror
+  return p;
+}
+
+// Over the whole wave; every lane receives the result.
+__device__ __forceinline__ uint32_t reduce_wave(uint32_t p) {
+  p = reduce_lanes16(p, 16);
+  const uint32_t a = pk_min((uint32_t)__builtin_amdgcn_readlane((int)p, 0),
+                            (uint32_t)__builtin_amdgcn_readlane((int)p, 16));
+  const uint32_t b = pk_min((uint32_t)__builtin_amdgcn_readlane((int)p, 32),
+                            (uint32_t)__builtin_amdgcn_readlane((int)p, 48));
+  return pk_min(a, b);
+}
+
+// Scale, zero point and the two-term reciprocal of the scale of one group.
+struct Params {
+  float r_hi, r_lo;  // r_hi + r_lo = 1/s
+  uint32_t zz;       // z - kRoundBits (mod 2^32): folds the rounding offset into the zero
+  uint32_t s16;      // stored scale (fp16 bits)
+  int z;             // stored zero point
+};
+
+// scale = fp16((max - min) / M), a zero scale replaced by 1, zero =
+// rint(-min / scale); every quotient equal to the correctly rounded fp32 one.
+template <int BITS>
+__device__ __forceinline__ Params group_params(uint32_t ext) {
+  constexpr float M = (float)((1 << BITS) - 1);
+  constexpr float m_hi = 1.0f / M;
+  constexpr float m_lo = (float)((1.0 - (double)M * (double)m_hi) * (double)m_hi);
+  const h2_t e = as_h2(ext);
+  const float lo = (float)e.x;
+  const float hi = -(float)e.y;
+  const float d = hi - lo;
+  float s32 = __builtin_fmaf(d, m_hi, d * m_lo);
+  // The scale is rounded twice: to fp32 (the quotient), then to fp16.  This
+  // empty barrier keeps the fp32 value: otherwise the fma and the conversion
+  // are folded into one mixed-precision fma that rounds once, straight to
+  // fp16, which differs when the fp32 quotient is an fp16 halfway case.
+  asm("" : "+v"(s32));
+  uint32_t s16 = f32_to_h_bits(s32);
+  if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;
+  const float s = h_bits_to_f32((uint16_t)s16);
+  Params p;
+  p.r_hi = 1.0f / s;
+  p.r_lo = __builtin_fmaf(-s, p.r_hi, 1.0f) * p.r_hi;
+  const float nl = -lo;
+  p.z = (int)__builtin_rintf(__builtin_fmaf(nl, p.r_hi, nl * p.r_lo));
+  p.zz = (uint32_t)p.z - kRoundBits;
+  p.s16 = s16;
+  return p;
+}
+
+// q = clamp(rint(w / s) + z, 0, M) for one fp16 weight.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(_Float16 wh, const Params& p) {
+  constexpr int M = (1 << BITS) - 1;
+  const float w = (float)wh;
+  // w * r_lo written as an fma with a zero addend so that it, too, takes the
+  // fp16 weight directly (the sign of a zero product cannot change the code)
+  const float v = __builtin_fmaf(w, p.r_hi, __builtin_fmaf(w, p.r_lo, 0.0f));
+  const uint32_t t = __builtin_bit_cast(uint32_t, v + kRoundMagic) + p.zz;
+  return (uint32_t)min(max((int)t, 0), M);
+}
+
+// The 8 codes of a chunk, packed least significant first.
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk_codes(const u4_t& d, const Params& p, uint32_t (&q)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 u = p[i];
-    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+    const h2_t v = as_h2(d[i]);
+    q[2 * i] = code_of<BITS>(v.x, p);
+    q[2 * i + 1] = code_of<BITS>(v.y, p);
+  }
+  uint32_t acc = q[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = h_bits_to_f32((uint16_t)(d[j] & 0xffffu));
-      v[8 * i + 2 * j + 1] = h_bits_to_f32((uint16_t)(d[j] >> 16));
+  for (int i = 1; i < 8; ++i) acc |= q[i] << (BITS * i);
+  return acc;
+}
+
+__device__ __forceinline__ u2_t code_bytes(const uint32_t (&q)[8]) {
+  u2_t b;
+  b[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+  b[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+  return b;
+}
+
+// Byte offset (within the row's packed words) of what this thread stores for
+// its chunk c = t (add `step` per further round of T chunks).  For 3-bit codes
+// the four lanes of a quad hold chunks 4m..4m+3, one 96-bit period: lane
+// j < 3 stores word j of the period; lane 3 gets an offset far past any row,
+// so the buffer unit drops its store.
+template <int BITS>
+struct StoreMap {
+  uint32_t off, step, shift;
+  __device__ __forceinline__ StoreMap(uint32_t t, uint32_t T) {
+    if constexpr (BITS == 4) {
+      off = t * 4u;
+      step = T * 4u;
+    } else if constexpr (BITS == 2) {
+      off = t * 2u;
+      step = T * 2u;
+    } else {
+      const uint32_t j = t & 3u;
+      off = j < 3u ? (3u * (t >> 2) + j) * 4u : 0x80000000u;
+      step = T * 3u;
+      shift = 8u + 8u * j;
     }
+  }
+};
+
+// Store a chunk's packed codes (`bits` holds its 8*BITS bits).  Every lane
+// of a quad must be active (3-bit codes exchange bits with the right
+// neighbour).  Stores past the buffer's end are dropped by the buffer unit.
+template <int BITS>
+__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t prs, uint32_t bits,
+                                            const StoreMap<BITS>& m, uint32_t i) {
+  const uint32_t off = m.off + i * m.step;
+  if constexpr (BITS == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(bits, prs, (int)off, 0, 0);
+  } else if constexpr (BITS == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bits, prs, (int)off, 0, 0);
+  } else {
+    const uint32_t next = dpp<0xf9>(bits);  // quad_perm [1,2,3,3]
+    const uint32_t word = __builtin_amdgcn_alignbit(next, bits << 8, m.shift);
+    __builtin_amdgcn_raw_buffer_store_b32(word, prs, (int)off, 0, 0);
   }
 }
 
-// One workgroup per row.  Three phases over the row:
-//  1. per-period min/max into LDS,
-//  2. per-group min/max -> (fp16 scale, int32 zero), written out and kept in LDS,
-//  3. codes: q = clamp(rint(w / s) + z, 0, M), written as bytes and/or packed.
-// Phase 3 re-reads the row, which the first phase has just brought into L2.
-template <int BITS>
-__global__ __launch_bounds__(kQuantThreads) void rtn_quantize_kernel(
-    const uint16_t* __restrict__ w, int K, int gp /* periods per group */, int G,
-    uint8_t* __restrict__ codes, uint32_t* __restrict__ packed, uint16_t* __restrict__ scales,
-    int32_t* __restrict__ zeros) {
-  constexpr int M = (1 << BITS) - 1;
-  extern __shared__ float smem[];
-  const int P = K >> 5;
-  float* plo = smem;
-  float* phi = smem + P;
-  float* gsc = smem + 2 * P;
-  int* gz = reinterpret_cast<int*>(smem + 2 * P + G);
-  __shared__ float red_lo[kQuantThreads / kWave];
-  __shared__ float red_hi[kQuantThreads / kWave];
+// One workgroup of T = blockDim.x threads per row; thread t owns chunks
+// c = i*T + t, i < NL.  Chunks past the row's end load zeros (buffer range
+// check), take no part in the extrema and store nothing.
+template <int BITS, int NL, int MODE, bool CODES>
+__global__ __launch_bounds__(1024) void rtn_quantize_kernel(
+    const uint16_t* __restrict__ w, int K, int G, int cpg /* chunks per group */,
+    int lg_cpg /* log2(cpg) when MODE == kLaneGroups */, uint8_t* __restrict__ codes,
+    uint32_t* __restrict__ packed, uint16_t* __restrict__ scales, int32_t* __restrict__ zeros) {
+  extern __shared__ uint32_t ent[];  // kLdsGroups: one (min, -max) pair per chunk
 
+  const int T = blockDim.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t >> 6;
+  const int waves = T >> 6;
+  const uint32_t C = (uint32_t)K >> 3;
   const int64_t row = blockIdx.x;
-  const uint16_t* wr = w + row * (int64_t)K;
-  const int tid = threadIdx.x;
+  const auto wrs = rsrc(w + row * K, (uint32_t)K * 2u);
+  const uint32_t row_words = (uint32_t)K * BITS / 32u;
+  const auto prs = rsrc(packed + row * row_words, packed ? row_words * 4u : 0u);
+  const auto crs = rsrc(codes + row * K, codes ? (uint32_t)K : 0u);
 
-  // phase 1
-  for (int p = tid; p < P; p += kQuantThreads) {
-    float v[32];
-    load_period_f32(wr + 32 * p, v);
-    float lo = v[0], hi = v[0];
+  u4_t d[NL];
 #pragma unroll
-    for (int c = 1; c < 32; ++c) {
-      lo = fminf(lo, v[c]);
-      hi = fmaxf(hi, v[c]);
-    }
-    plo[p] = lo;
-    phi[p] = hi;
-  }
-  __syncthreads();
+  for (int i = 0; i < NL; ++i)
+    d[i] = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)((uint32_t)(i * T + t) * 16u), 0, kSlc);
 
-  // phase 2
-  auto finish_group = [&](int j, float lo, float hi) {
-    const float d = hi - lo;
-    const float s32 = d / (float)M;
-    uint16_t s16 = f32_to_h_bits(s32);
-    if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;
-    const float s = h_bits_to_f32(s16);
-    const int z = (int)__builtin_rintf(-lo / s);
-    scales[row * G + j] = s16;
-    zeros[row * G + j] = z;
-    gsc[j] = s;
-    gz[j] = z;
+  // Codes of chunk i.  Without a packed output the buffer range is empty and
+  // the packed stores are dropped; byte codes are a compile-time choice.
+  const StoreMap<BITS> smap((uint32_t)t, (uint32_t)T);
+  auto emit = [&](int i, const Params& p) {
+    uint32_t q[8];
+    const uint32_t bits = chunk_codes<BITS>(d[i], p, q);
+    if constexpr (CODES)
+      __builtin_amdgcn_raw_buffer_store_b64(code_bytes(q), crs, (int)((uint32_t)(i * T + t) * 8u),
+                                            0, 0);
+    store_chunk<BITS>(prs, bits, smap, (uint32_t)i);
   };
-  if (gp <= 16) {
-    for (int j = tid; j < G; j += kQuantThreads) {
-      float lo = plo[j * gp], hi = phi[j * gp];
-      for (int p = 1; p < gp; ++p) {
-        lo = fminf(lo, plo[j * gp + p]);
-        hi = fmaxf(hi, phi[j * gp + p]);
+
+  if constexpr (MODE == kRowGroup) {
+    __shared__ uint32_t wave_ext[16];
+    uint32_t lo = kPosInfPair, hi = kPosInfPair ^ 0x80008000u;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if ((uint32_t)(i * T + t) < C) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo = pk_min_raw(lo, d[i][k]);
+          hi = pk_max_raw(hi, d[i][k]);
+        }
       }
-      finish_group(j, lo, hi);
+    }
+    const h2_t l = as_h2(lo), h = as_h2(hi);
+    h2_t e;
+    e.x = __builtin_elementwise_min(l.x, l.y);
+    e.y = -__builtin_elementwise_max(h.x, h.y);
+    uint32_t ext = reduce_wave(as_u32(e));
+    if (waves > 1) {
+      if (lane == 0) wave_ext[wave] = ext;
+      __syncthreads();
+      ext = wave_ext[0];
+      for (int k = 1; k < waves; ++k) ext = pk_min(ext, wave_ext[k]);
+    }
+    const Params p = group_params<BITS>(ext);
+    if (t == 0) {
+      scales[row] = (uint16_t)p.s16;
+      zeros[row] = p.z;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) emit(i, p);
+  } else if constexpr (MODE == kLaneGroups) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t c = (uint32_t)(i * T + t);
+      uint32_t ext = reduce_lanes16(chunk_extrema(d[i]), cpg);
+      if (cpg >= 32) ext = pk_min(ext, (uint32_t)__builtin_amdgcn_ds_swizzle((int)ext, 0x401F));
+      if (cpg >= 64)
+        ext = pk_min((uint32_t)__builtin_amdgcn_readlane((int)ext, 0),
+                     (uint32_t)__builtin_amdgcn_readlane((int)ext, 32));
+      const Params p = group_params<BITS>(ext);
+      if ((lane & (cpg - 1)) == 0 && c < C) {
+        const int64_t j = row * G + (c >> lg_cpg);
+        scales[j] = (uint16_t)p.s16;
+        zeros[j] = p.z;
+      }
+      emit(i, p);
     }
   } else {
-    const int wave = tid / kWave, lane = tid % kWave;
-    for (int j = 0; j < G; ++j) {
-      float lo = INFINITY, hi = -INFINITY;
-      for (int p = tid; p < gp; p += kQuantThreads) {
-        lo = fminf(lo, plo[j * gp + p]);
-        hi = fmaxf(hi, phi[j * gp + p]);
-      }
-      lo = wave_min(lo);
-      hi = wave_max(hi);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t c = (uint32_t)(i * T + t);
+      if (c < C) ent[c] = chunk_extrema(d[i]);
+    }
+    __syncthreads();
+    // A wave per group.  Its three parameters then overwrite the group's
+    // first entries (cpg >= 12 here), which only this wave reads.
+    for (int j = wave; j < G; j += waves) {
+      uint32_t ext = kPosInfPair;
+      for (int e = lane; e < cpg; e += kWave) ext = pk_min(ext, ent[j * cpg + e]);
+      ext = reduce_wave(ext);
+      const Params p = group_params<BITS>(ext);
       if (lane == 0) {
-        red_lo[wave] = lo;
-        red_hi[wave] = hi;
+        scales[row * G + j] = (uint16_t)p.s16;
+        zeros[row * G + j] = p.z;
+        ent[j * cpg] = __builtin_bit_cast(uint32_t, p.r_hi);
+        ent[j * cpg + 1] = __builtin_bit_cast(uint32_t, p.r_lo);
+        ent[j * cpg + 2] = p.zz;
       }
-      __syncthreads();
-      if (tid == 0) {
-        for (int i = 1; i < kQuantThreads / kWave; ++i) {
-          lo = fminf(lo, red_lo[i]);
-          hi = fmaxf(hi, red_hi[i]);
-        }
-        finish_group(j, lo, hi);
-      }
-      __syncthreads();
     }
-  }
-  __syncthreads();
-
-  // phase 3
-  const int64_t wpr = (int64_t)K * BITS / 32;  // packed words per row
-  for (int p = tid; p < P; p += kQuantThreads) {
-    const int j = p / gp;
-    const float s = gsc[j];
-    const int z = gz[j];
-    float v[32];
-    load_period_f32(wr + 32 * p, v);
-    uint32_t q[32];
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      const int t = (int)__builtin_rintf(v[c] / s) + z;
-      q[c] = (uint32_t)min(max(t, 0), M);
-    }
-    if (codes) {
-      uint32_t b[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        b[i] = q[4 * i] | (q[4 * i + 1] << 8) | (q[4 * i + 2] << 16) | (q[4 * i + 3] << 24);
-      uint4* dst = reinterpret_cast<uint4*>(codes + row * (int64_t)K + 32 * p);
-      dst[0] = make_uint4(b[0], b[1], b[2], b[3]);
-      dst[1] = make_uint4(b[4], b[5], b[6], b[7]);
-    }
-    if (packed) {
-      uint32_t wd[BITS];
-      pack_period<BITS>(q, wd);
-      store_packed<BITS>(packed + row * wpr + (int64_t)BITS * p, wd);
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t c = (uint32_t)(i * T + t);
+      const uint32_t j = min(c / (uint32_t)cpg, (uint32_t)G - 1u);
+      Params p;
+      p.r_hi = __builtin_bit_cast(float, ent[j * cpg]);
+      p.r_lo = __builtin_bit_cast(float, ent[j * cpg + 1]);
+      p.zz = ent[j * cpg + 2];
+      emit(i, p);
     }
   }
 }
 
-// One thread per 32-code period of the whole [N][K] code matrix.
+// Packs byte codes: chunk c of the whole [N][K] matrix (8 codes, one 64-bit
+// load) lands at the same place of the concatenated packed rows, because
+// every row holds a whole number of chunks and (for 3-bit) of 4-chunk periods.
 template <int BITS>
-__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t nper,
-                                                   uint32_t* __restrict__ packed) {
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes,
+                                                   int64_t nchunks, uint32_t* __restrict__ packed) {
   constexpr uint32_t mask = (1u << BITS) - 1u;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nper;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const uint4* src = reinterpret_cast<const uint4*>(codes + 32 * i);
-    const uint4 a = src[0], b = src[1];
-    const uint32_t by[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t q[32];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // nchunks is a multiple of 4, so quads of lanes are active or idle together
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+    const u2_t b = *reinterpret_cast<const u2_t*>(codes + 8 * c);
+    uint32_t bits = 0;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) q[c] = (by[c >> 2] >> (8 * (c & 3))) & mask;
-    uint32_t wd[BITS];
-    pack_period<BITS>(q, wd);
-    store_packed<BITS>(packed + BITS * i, wd);
+    for (int i = 0; i < 8; ++i) bits |= ((b[i >> 2] >> (8 * (i & 3))) & mask) << (BITS * i);
+    if constexpr (BITS == 4) {
+      packed[c] = bits;
+    } else if constexpr (BITS == 2) {
+      reinterpret_cast<uint16_t*>(packed)[c] = (uint16_t)bits;
+    } else {
+      const uint32_t next = dpp<0xf9>(bits);  // quad_perm [1,2,3,3]
+      const uint32_t j = (uint32_t)lane & 3u;
+      const uint32_t word = __builtin_amdgcn_alignbit(next, bits << 8, 8u + 8u * j);
+      if (j < 3u) packed[3 * (c >> 2) + j] = word;
+    }
   }
+}
+
+constexpr int kChunkCounts[] = {1, 2, 4, 6, 8, 16};
+
+template <int BITS, int MODE>
+hipError_t launch_mode(const uint16_t* w, int64_t N, int K, int G, int cpg, int lg_cpg, int T,
+                       int nl, size_t lds, uint8_t* codes, uint32_t* packed, uint16_t* scales,
+                       int32_t* zeros, hipStream_t stream) {
+  const dim3 grid((unsigned)N), block((unsigned)T);
+#define LOWBIT_Q_NL(n)                                                                      \
+  case n:                                                                                   \
+    if (codes)                                                                              \
+      hipLaunchKernelGGL((rtn_quantize_kernel<BITS, n, MODE, true>), grid, block, lds, stream, \
+                         w, K, G, cpg, lg_cpg, codes, packed, scales, zeros);               \
+    else                                                                                    \
+      hipLaunchKernelGGL((rtn_quantize_kernel<BITS, n, MODE, false>), grid, block, lds,       \
+                         stream, w, K, G, cpg, lg_cpg, codes, packed, scales, zeros);       \
+    break;
+  switch (nl) {
+    LOWBIT_Q_NL(1)
+    LOWBIT_Q_NL(2)
+    LOWBIT_Q_NL(4)
+    LOWBIT_Q_NL(6)
+    LOWBIT_Q_NL(8)
+    LOWBIT_Q_NL(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef LOWBIT_Q_NL
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const uint16_t* w, int64_t N, int K, int G, int cpg, int T, int nl,
+                       uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
+                       hipStream_t stream) {
+  const bool pow2 = (cpg & (cpg - 1)) == 0;
+  if (G == 1)
+    return launch_mode<BITS, kRowGroup>(w, N, K, G, cpg, 0, T, nl, 0, codes, packed, scales,
+                                        zeros, stream);
+  if (pow2 && cpg <= kWave) {
+    int lg = 0;
+    while ((1 << lg) < cpg) ++lg;
+    return launch_mode<BITS, kLaneGroups>(w, N, K, G, cpg, lg, T, nl, 0, codes, packed, scales,
+                                          zeros, stream);
+  }
+  const size_t lds = (size_t)(K / 8) * 4;
+  return launch_mode<BITS, kLdsGroups>(w, N, K, G, cpg, 0, T, nl, lds, codes, packed, scales,
+                                       zeros, stream);
 }
 
 }  // namespace
-
-size_t quantize_lds_bytes(int64_t K, int64_t G) { return (size_t)(2 * (K / 32) + 2 * G) * 4; }
 
 hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t gsz,
                            uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
                            hipStream_t stream) {
   const int64_t g = gsz == 0 ? K : gsz;
-  const int64_t G = K / g;
-  const int gp = (int)(g / 32);
-  const size_t lds = quantize_lds_bytes(K, G);
-  const dim3 grid((unsigned)N), block(kQuantThreads);
+  const int G = (int)(K / g);
+  const int cpg = (int)(g / 8);
+  const int64_t C = K / 8;
+  // Threads per row: enough that a thread owns at most 8 chunks (16 when the
+  // 1024-thread limit binds); at least one wave.
+  int T = kWave;
+  while (T < 1024 && (int64_t)T * 8 < C) T *= 2;
+  const int need = (int)((C + T - 1) / T);
+  int nl = 0;
+  for (int n : kChunkCounts)
+    if (n >= need) {
+      nl = n;
+      break;
+    }
+  if (nl == 0) return hipErrorInvalidValue;
   switch (bits) {
     case 2:
-      hipLaunchKernelGGL(rtn_quantize_kernel<2>, grid, block, lds, stream, w, (int)K, gp, (int)G,
-                         codes, packed, scales, zeros);
-      break;
+      return launch_bits<2>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
     case 3:
-      hipLaunchKernelGGL(rtn_quantize_kernel<3>, grid, block, lds, stream, w, (int)K, gp, (int)G,
-                         codes, packed, scales, zeros);
-      break;
+      return launch_bits<3>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
     default:
-      hipLaunchKernelGGL(rtn_quantize_kernel<4>, grid, block, lds, stream, w, (int)K, gp, (int)G,
-                         codes, packed, scales, zeros);
-      break;
+      return launch_bits<4>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
                        hipStream_t stream) {
-  const int64_t nper = N * (K / 32);
-  const int64_t want = (nper + 255) / 256;
+  const int64_t nchunks = N * (K / 8);
+  const int64_t want = (nchunks + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 16;
   const dim3 grid((unsigned)(want < cap ? want : cap)), block(256);
   switch (bits) {
     case 2:
-      hipLaunchKernelGGL(pack_kernel<2>, grid, block, 0, stream, codes, nper, packed);
+      hipLaunchKernelGGL(pack_kernel<2>, grid, block, 0, stream, codes, nchunks, packed);
       break;
     case 3:
-      hipLaunchKernelGGL(pack_kernel<3>, grid, block, 0, stream, codes, nper, packed);
+      hipLaunchKernelGGL(pack_kernel<3>, grid, block, 0, stream, codes, nchunks, packed);
       break;
     default:
-      hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, stream, codes, nper, packed);
+      hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, stream, codes, nchunks, packed);
       break;
   }
   return hipGetLastError();
