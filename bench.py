@@ -101,8 +101,9 @@ def run_product(lw, prep: Prepared, B: int, c: int, stream: int, kernel: str) ->
         raise RuntimeError(f"{kernel} failed: {lw.status_string(st)}")
 
 
-def time_launches(torch, fn, count: int):
-    """Average device time of `count` launches of fn(i), each bracketed by events."""
+def time_launches(torch, fn, count: int, spread: bool = False):
+    """Device time of `count` launches of fn(i), each bracketed by events:
+    (average, median) in ms, and with spread=True also (p10, p90)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(count)]
     for i, (a, b) in enumerate(evs):
@@ -111,7 +112,10 @@ def time_launches(torch, fn, count: int):
         b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ms) / len(ms), ms[len(ms) // 2]
+    avg, med = sum(ms) / len(ms), ms[len(ms) // 2]
+    if not spread:
+        return avg, med
+    return avg, med, ms[(len(ms) - 1) // 10], ms[(9 * (len(ms) - 1)) // 10]
 
 
 def measure_stages(lw, torch, stream: int, reps: int) -> dict:
@@ -134,10 +138,11 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
                 raise RuntimeError(lw.status_string(st))
 
         q(0)
-        avg, med = time_launches(torch, q, reps)
+        avg, med, p10, p90 = time_launches(torch, q, reps, spread=True)
         nbytes = quantize_bytes(layer.N, layer.K, layer.bits, layer.group_size)
         stages[f"quantize_pack/{layer.name}"] = {
-            "us": round(avg * 1e3, 2), "bytes": nbytes,
+            "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2),
+            "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2), "bytes": nbytes,
             "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
         del w, packed, scales, zeros
@@ -152,11 +157,12 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
                     prep = Prepared(lw, torch, layer, copies_for(fp))
                 for i in range(3):
                     run_product(lw, prep, B, i, stream, kern)
-                avg, med = time_launches(
-                    torch, lambda i: run_product(lw, prep, B, i, stream, kern), reps)
+                avg, med, p10, p90 = time_launches(
+                    torch, lambda i: run_product(lw, prep, B, i, stream, kern), reps, spread=True)
                 nbytes = product_bytes(layer.N, layer.K, layer.bits, layer.group_size, B)
                 gbps = nbytes / (avg * 1e-3) / 1e9
                 rec = {"kernel": kern, "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2),
+                       "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
                        "bytes": nbytes, "GBps": round(gbps, 1),
                        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
                 if kern == "qgemm":
@@ -166,6 +172,19 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
                 stages[f"{kern}/{layer.name}/B{B}"] = rec
             del prep
             torch.cuda.empty_cache()
+    # a measured streaming reference next to the published peak: a plain
+    # device-to-device copy (read + write) of 1 GiB
+    src = torch.empty(COPY_REF_BYTES // 2, dtype=torch.float16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    avg, med, p10, p90 = time_launches(torch, lambda i: dst.copy_(src), 10, spread=True)
+    moved = 2 * COPY_REF_BYTES
+    stages["reference/device_copy_1GiB"] = {
+        "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2), "bytes_read_plus_written": moved,
+        "GBps": round(moved / (avg * 1e-3) / 1e9, 1),
+        "hbm_frac": round(moved / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
     return stages
 
 
@@ -216,13 +235,17 @@ def load_traffic(avg_bytes_per_launch: int):
 
 
 COPY_BYTES = 256 << 20
+COPY_REF_BYTES = 1 << 30
 
 
 def counter_pass(lw, torch, layers, stream: int) -> int:
-    """Launch sequence profiled by the FETCH_SIZE / WRITE_SIZE passes: three GEMV
-    launches per layer (distinct weight copies), then three plain device-to-device
-    copies of COPY_BYTES whose counter readings calibrate the bytes per count."""
-    preps = [Prepared(lw, torch, L, 3) for L in layers]
+    """Launch sequence profiled by the counter passes (FETCH_SIZE, WRITE_SIZE,
+    MfmaUtil / VALUBusy): the quantizer once per GEMV layer, three GEMV launches
+    per layer (distinct weight copies), two matrix-core launches per batch of
+    the Llama-70B MLP shape, then three plain device-to-device copies of
+    COPY_BYTES whose counter readings calibrate the bytes per count."""
+    import synth
+    preps = [Prepared(lw, torch, L, 3) for L in layers]  # quantizes each layer once
     for p in preps:
         del p.w
     torch.cuda.synchronize()
@@ -230,6 +253,14 @@ def counter_pass(lw, torch, layers, stream: int) -> int:
         for i in range(3):
             run_product(lw, p, 1, i, stream, "qgemv")
     torch.cuda.synchronize()
+    big = synth.WORKLOADS["llama70b_mlp_4bit"][0]
+    pg = Prepared(lw, torch, big, 2)
+    del pg.w
+    for B in big.batches:
+        for i in range(2):
+            run_product(lw, pg, B, i, stream, "qgemm")
+    torch.cuda.synchronize()
+    del pg
     src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device="cuda:0").normal_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -238,6 +269,11 @@ def counter_pass(lw, torch, layers, stream: int) -> int:
     torch.cuda.synchronize()
     per_launch = {p.layer.name: product_bytes(p.layer.N, p.layer.K, p.layer.bits,
                                               p.layer.group_size, 1) for p in preps}
+    for B in big.batches:
+        per_launch[f"{big.name}/B{B}"] = product_bytes(big.N, big.K, big.bits, big.group_size, B)
+    for p in preps:
+        L = p.layer
+        per_launch[f"quantize/{L.name}"] = quantize_bytes(L.N, L.K, L.bits, L.group_size)
     print(json.dumps({"counter_pass": True, "copy_bytes": COPY_BYTES,
                       "algorithmic_bytes_per_launch": per_launch}), flush=True)
     return 0
@@ -252,8 +288,9 @@ def main() -> int:
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--counter-pass", action="store_true",
-                    help="for rocprofv3 --pmc: a few GEMV launches on both layers, then a plain "
-                         "device copy of COPY_BYTES (the counters' calibration), nothing else")
+                    help="for rocprofv3 --pmc: the quantizer and a few GEMV launches on both "
+                         "layers, a few matrix-core launches of the Llama-70B MLP shape, then a "
+                         "plain device copy of COPY_BYTES (the counters' calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
