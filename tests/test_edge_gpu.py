@@ -242,6 +242,22 @@ def test_qgemm_shapes(lw, bits, N, K, g):
     _check_product(lw, w, bits, g, [1, 16, 17, 33, 64, 70], "qgemm")
 
 
+# Groups at least as long as one lane's units of a matrix-core step (2- and
+# 4-bit, g >= 128), with K not a multiple of the 512-long step: the last step
+# of every row runs past the row end.
+WIDE_GROUP_CASES = [(4, 33, 640, 128), (4, 17, 1280, 256), (2, 9, 640, 128), (2, 21, 1408, 128),
+                    (4, 40, 2176, 128)]
+
+
+@pytest.mark.parametrize("bits,N,K,g", WIDE_GROUP_CASES)
+@pytest.mark.parametrize("kind", ["normal", "mixed"])
+def test_products_wide_groups_ragged(lw, bits, N, K, g, kind):
+    _say(f"[wide groups] bits={bits} N={N} K={K} g={g} {kind}")
+    w = _weights(kind, N, K, seed=N + 11 * K + bits)
+    _check_product(lw, w, bits, g, [1, 16, 17, 33, 64], "qgemm")
+    _check_product(lw, w, bits, g, [1, 4], "qgemv")
+
+
 @pytest.mark.parametrize("kind", ["wide", "tiny", "offset", "mixed", "positive", "negative", "ties"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_products_degenerate(lw, kind, bits):

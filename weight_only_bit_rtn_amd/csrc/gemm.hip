@@ -287,6 +287,25 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     auto compute = [&](int t, int buf, WBuf& b) {
       if (!active) return;
       const uint4* xs = lds + buf * XBUF;
+      // one group for all of the lane's units of the step: its constants are
+      // made once per step, with every position valid.  Positions past the
+      // row end (last step of a ragged row) then decode the clamped words
+      // against zero activations: only a finite decode is needed there, which
+      // the fast path's zero-point range and s < 4096 guarantee
+      // (|q - z| * s <= 15 * s < 65504).  The exact path keeps the per-unit
+      // validity.
+      Consts<BITS> wcc[NC];
+      bool wfast = true;
+      if constexpr (GM == kWideGroups) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          HalfParams h0 = b.hp[0][c];
+          h0.v_lo = true;
+          h0.v_hi = true;
+          wfast &= make_consts<BITS, false>(h0, wcc[c]);
+          wfast &= h0.s_lo < 0x6C00u && h0.s_hi < 0x6C00u;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < NWMAX; ++u) {
         if (u < NW) {
@@ -303,15 +322,20 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
               cc[c] = rowc;
             }
             fast = rowfast;
+          } else if constexpr (GM == kWideGroups) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              hp[c] = b.hp[0][c];  // the shared group; this unit's validity
+              hp[c].v_lo = ur.va;
+              hp[c].v_hi = ur.vb;
+              cc[c] = wcc[c];
+            }
+            fast = wfast;
           } else {
             fast = true;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-              hp[c] = b.hp[GM == kWideGroups ? 0 : u][c];
-              if constexpr (GM == kWideGroups) {  // the shared group; this unit's validity
-                hp[c].v_lo = ur.va;
-                hp[c].v_hi = ur.vb;
-              }
+              hp[c] = b.hp[u][c];
               fast &= make_consts<BITS, false>(hp[c], cc[c]);
             }
           }
