@@ -54,12 +54,13 @@ class Oracle:
         lib.orc_f64_to_f16.argtypes = [ctypes.c_double]
         lib.orc_f64_to_f16.restype = ctypes.c_uint16
         lib.orc_quantize_rtn.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp]
+        lib.orc_quantize_rtn_sym.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp]
         lib.orc_pack.argtypes = [vp, i64, i64, i32, vp]
         lib.orc_unpack.argtypes = [vp, i64, i64, i32, vp]
         lib.orc_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i64, vp]
         lib.orc_matmul_f64.argtypes = [vp, vp, i64, i64, i64, vp]
-        for name in ("orc_quantize_rtn", "orc_pack", "orc_unpack", "orc_dequant",
-                     "orc_matmul_f64"):
+        for name in ("orc_quantize_rtn", "orc_quantize_rtn_sym", "orc_pack", "orc_unpack",
+                     "orc_dequant", "orc_matmul_f64"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -84,6 +85,20 @@ class Oracle:
         _ok(self.lib.orc_quantize_rtn(wb.ctypes.data, N, K, bits, group_size,
                                       codes.ctypes.data, scales.ctypes.data,
                                       zeros.ctypes.data), "quantize_rtn")
+        return codes, scales.view(np.float16), zeros
+
+    def quantize_rtn_sym(self, w: np.ndarray, bits: int, group_size: int):
+        """Signed symmetric RTN quantization of fp16 ``w[N][K]`` (codes stored
+        with the zero point 2^(bits-1)); same outputs as ``quantize_rtn``."""
+        wb = _bits16(w)
+        N, K = wb.shape
+        G = groups(K, group_size)
+        codes = np.empty((N, K), np.uint8)
+        scales = np.empty((N, G), np.uint16)
+        zeros = np.empty((N, G), np.int32)
+        _ok(self.lib.orc_quantize_rtn_sym(wb.ctypes.data, N, K, bits, group_size,
+                                          codes.ctypes.data, scales.ctypes.data,
+                                          zeros.ctypes.data), "quantize_rtn_sym")
         return codes, scales.view(np.float16), zeros
 
     def pack(self, codes: np.ndarray, bits: int) -> np.ndarray:
@@ -139,7 +154,8 @@ def default() -> Oracle:
     global _DEFAULT
     if _DEFAULT is None:
         path = _build.library_path()
-        if not os.path.exists(path):
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lowbit_oracle.c")
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
             _build.build()
         _DEFAULT = Oracle(path)
     return _DEFAULT
@@ -155,6 +171,10 @@ def f64_to_f16(v):
 
 def quantize_rtn(w, bits, group_size):
     return default().quantize_rtn(w, bits, group_size)
+
+
+def quantize_rtn_sym(w, bits, group_size):
+    return default().quantize_rtn_sym(w, bits, group_size)
 
 
 def pack(codes, bits):

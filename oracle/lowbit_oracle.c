@@ -158,6 +158,57 @@ int orc_quantize_rtn(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t 
 }
 
 /* ---------------------------------------------------------------------- */
+/* Signed symmetric variant (reading R14).  BladeLLM's weight-only modes    */
+/* are "signed symmetric" by default (BladeLLM model quantization,          */
+/* "Quantization modes"), and the GGUF Q4_0 / Q8_0 types reconstruct a      */
+/* weight as code times block scale (GGUF, quantization type table).  The   */
+/* grid is centred on zero: with qmax = 2^(b-1) - 1,                        */
+/*   s = fp16(fl32(max |w| / qmax)), a zero scale replaced by 1.0,          */
+/*   q = clamp(rint(w / s), -qmax, qmax)  (half to even),                   */
+/* stored as the code q + 2^(b-1) with the zero point 2^(b-1), so that the   */
+/* dequantized weight (code - zero) * s is q * s and the packed form and    */
+/* the products are those of the asymmetric mode.                           */
+/* ---------------------------------------------------------------------- */
+int orc_quantize_rtn_sym(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
+                         uint8_t* codes, uint16_t* scales, int32_t* zeros) {
+    if (!w || !codes || !scales || !zeros || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
+    if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return -1;
+    const int64_t gs = group_size == 0 ? K : group_size;
+    const int64_t ng = groups_of(K, group_size);
+    const int qmax = (1 << (bits - 1)) - 1;
+    const int32_t z = 1 << (bits - 1);
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < ng; ++j) {
+            const uint16_t* wr = w + n * K + j * gs;
+            /* step 1: the group's largest magnitude (fp16 -> fp32 is exact) */
+            float amax = 0.0f;
+            for (int64_t k = 0; k < gs; ++k) {
+                float a = fabsf((float)orc_f16_to_f64(wr[k]));
+                if (a > amax) amax = a;
+            }
+            /* step 2: scale = max|w| / qmax in fp32, stored as fp16; 0 -> 1.0 */
+            float sq = amax / (float)qmax;
+            uint16_t sh = orc_f64_to_f16((double)sq);
+            if ((sh & 0x7fff) == 0) sh = 0x3c00;
+            float sc = (float)orc_f16_to_f64(sh);
+            scales[n * ng + j] = sh;
+            zeros[n * ng + j] = z;
+            /* step 3: q = clamp(rint(w / s), -qmax, qmax), code = q + zero */
+            for (int64_t k = 0; k < gs; ++k) {
+                float v = (float)orc_f16_to_f64(wr[k]);
+                float r = nearbyintf(v / sc);
+                int64_t q = (int64_t)r;
+                if (q < -qmax) q = -qmax;
+                if (q > qmax) q = qmax;
+                codes[n * K + j * gs + k] = (uint8_t)(q + z);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Packing (reading R5): code k of a row sits at bit b*k of the row's      */
 /* little-endian bitstream.                                                */
 /* ---------------------------------------------------------------------- */

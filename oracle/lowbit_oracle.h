@@ -31,6 +31,8 @@ uint16_t orc_f64_to_f16(double v);
 
 int orc_quantize_rtn(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
                      uint8_t* codes, uint16_t* scales, int32_t* zeros);
+int orc_quantize_rtn_sym(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
+                         uint8_t* codes, uint16_t* scales, int32_t* zeros);
 int orc_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed);
 int orc_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* codes);
 int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,

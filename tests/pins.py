@@ -283,6 +283,106 @@ def check_rtn_bruteforce(o) -> None:
 
 
 # ---------------------------------------------------------------------------
+# Signed symmetric variant (zero point fixed at 2^(b-1))
+# ---------------------------------------------------------------------------
+def check_sym_worked_examples(o) -> None:
+    for case in _load("rtn_sym_worked_examples.json")["cases"]:
+        w = np.array([case["w"]], np.float16)
+        codes, scales, zeros = o.quantize_rtn_sym(w, case["bits"], 0)
+        name = case["name"]
+        assert scales.view(np.uint16)[0, 0] == int(case["scale_f16_bits"], 16), name
+        assert zeros[0, 0] == case["zero"], name
+        assert codes[0].tolist() == case["codes"], name
+        deq = o.dequant(codes, scales, zeros, case["bits"], 0)
+        assert deq[0].astype(np.float64).tolist() == case["deq"], name
+
+
+def check_sym_invariants(o) -> None:
+    """Zero point 2^(b-1); codes in [1, 2^b - 1]; the largest magnitude maps to
+    the end of the grid with its sign; quantizing -w mirrors the codes about
+    the zero point (round-half-even is odd-symmetric); bounded reconstruction
+    error."""
+    rng = np.random.default_rng(4242)
+    for label, w in _random_weight_sets(rng):
+        N, K = w.shape
+        wf = w.astype(np.float64)
+        for bits in (2, 3, 4):
+            M, z, qmax = (1 << bits) - 1, 1 << (bits - 1), (1 << (bits - 1)) - 1
+            for g in (0, 32, 128):
+                codes, scales, zeros = o.quantize_rtn_sym(w, bits, g)
+                neg_codes, neg_scales, _ = o.quantize_rtn_sym(-w, bits, g)
+                assert np.all(zeros == z), (label, bits, g, "zero point")
+                assert codes.min() >= 1 and codes.max() <= M, (label, bits, g, "code range")
+                assert np.array_equal(neg_scales.view(np.uint16), scales.view(np.uint16))
+                assert np.array_equal(neg_codes.astype(int), 2 * z - codes.astype(int)), \
+                    (label, bits, g, "mirror")
+                gs = K if g == 0 else g
+                deq = o.dequant(codes, scales, zeros, bits, g).astype(np.float64)
+                for n in range(N):
+                    for j in range(K // gs):
+                        seg = slice(j * gs, (j + 1) * gs)
+                        wseg = wf[n, seg]
+                        i = int(np.argmax(np.abs(wseg)))
+                        if wseg[i] != 0:
+                            want = z + qmax if wseg[i] > 0 else z - qmax
+                            assert codes[n, seg][i] == want, (label, bits, g, "extreme code")
+                        sj = float(scales[n, j])
+                        err = np.abs(deq[n, seg] - wseg)
+                        ulp = np.spacing(np.abs(deq[n, seg]).astype(np.float16)).astype(np.float64)
+                        bound = sj * (0.5 + qmax * 2.0 ** -10) + ulp / 2 + np.abs(wseg) * 2.0 ** -22
+                        assert np.all(err <= bound), (label, bits, g, "reconstruction error")
+
+
+def check_sym_scale_is_nearest(o) -> None:
+    """The stored scale is the fp16 nearest to the fp32 quotient max|w| / qmax
+    (one IEEE fp32 division, numpy float32), found by exact rational search;
+    a zero result is stored as 1.0."""
+    rng = np.random.default_rng(606)
+    for label, w in _random_weight_sets(rng):
+        for bits in (2, 3, 4):
+            qmax = (1 << (bits - 1)) - 1
+            for g in (0, 64):
+                _, scales, _ = o.quantize_rtn_sym(w, bits, g)
+                N, K = w.shape
+                gs = K if g == 0 else g
+                sb = scales.view(np.uint16)
+                for n in range(0, N, 3):
+                    for j in range(0, K // gs, 2):
+                        amax = np.float32(np.abs(w[n, j * gs:(j + 1) * gs].astype(np.float32)).max())
+                        q32 = amax / np.float32(qmax)
+                        want = _nearest_f16_bits(Fraction(float(q32)))
+                        if want & 0x7FFF == 0:
+                            want = 0x3C00
+                        assert sb[n, j] == want, (label, bits, g, hex(sb[n, j]), hex(want))
+
+
+def check_sym_bruteforce(o) -> None:
+    """Every code, less the zero point, is the grid level of [-qmax, qmax]
+    nearest the fp32 quotient w / s (ties to the even level)."""
+    rng = np.random.default_rng(8080)
+    for trial in range(45):
+        bits = (2, 3, 4)[trial % 3]
+        z, qmax = 1 << (bits - 1), (1 << (bits - 1)) - 1
+        g = (0, 2, 4)[(trial // 3) % 3]
+        w = (rng.standard_normal((4, 8)) * rng.choice([0.02, 1.0, 40.0])).astype(np.float16)
+        if trial % 5 == 0:
+            w[2, :4] = 0
+        codes, scales, zeros = o.quantize_rtn_sym(w, bits, g)
+        gs = 8 if g == 0 else g
+        for n in range(4):
+            for j in range(8 // gs):
+                s32 = np.float32(scales[n, j])
+                for k in range(gs):
+                    t = Fraction(float(np.float32(w[n, j * gs + k]) / s32))
+                    best = None
+                    for q in range(-qmax, qmax + 1):
+                        key = (abs(Fraction(q) - t), q & 1)
+                        if best is None or key < best[0]:
+                            best = (key, q)
+                    assert codes[n, j * gs + k] == best[1] + z, ("sym code", trial, n, j, k)
+
+
+# ---------------------------------------------------------------------------
 # The reference product against exact integer arithmetic
 # ---------------------------------------------------------------------------
 def check_matmul_exact(o) -> None:
@@ -310,7 +410,8 @@ def check_matmul_exact(o) -> None:
                            atol=1e-300)
 
 
-ALL_CHECKS = [check_f16_decode, check_f16_encode, check_worked_examples,
+ALL_CHECKS = [check_sym_worked_examples, check_sym_invariants, check_sym_scale_is_nearest,
+              check_sym_bruteforce, check_f16_decode, check_f16_encode, check_worked_examples,
               check_pack_closed_forms, check_pack_bigint, check_invariants,
               check_scale_is_nearest, check_dequant_is_nearest, check_rtn_bruteforce,
               check_matmul_exact]

@@ -38,6 +38,13 @@ MUTANTS = {
     "f16_decode_wrong_bias": ("v = ldexp((double)(1024 + f), e - 25);",
                               "v = ldexp((double)(1024 + f), e - 24);"),
     "matmul_transposed": ("orc_f16_to_f64(deq[n * K + k])", "orc_f16_to_f64(deq[k * N + n])"),
+    "sym_divisor_power_of_two": ("const int qmax = (1 << (bits - 1)) - 1;",
+                                 "const int qmax = (1 << (bits - 1));"),
+    "sym_no_absolute_value": ("float a = fabsf((float)orc_f16_to_f64(wr[k]));",
+                              "float a = (float)orc_f16_to_f64(wr[k]);"),
+    "sym_zero_off_by_one": ("const int32_t z = 1 << (bits - 1);",
+                            "const int32_t z = (1 << (bits - 1)) - 1;"),
+    "sym_round_half_away": ("float r = nearbyintf(v / sc);", "float r = roundf(v / sc);"),
 }
 
 
