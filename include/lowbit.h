@@ -97,6 +97,24 @@ LOWBIT_API int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int 
                         int32_t* zeros, void* hip_stream);
 
 /*
+ * Quantize w[N][K] onto the signed symmetric grid, the other RTN mode
+ * (BladeLLM model quantization, "Quantization modes": symmetric quantization
+ * keeps no zero point; GGUF file format, the quantization-type table: the
+ * "legacy" x = d*q types).  Per group, with qmax = 2^(bits-1) - 1:
+ *    amax = max |w| (fp32, exact); s16 = fp16_rne(fl32(amax / qmax)),
+ *    replaced by 1.0 when it is zero; s = (float)s16;
+ *    q = clamp((int) rint(fl32(w / s)), -qmax, qmax), rint half to even.
+ * The stored code is q + 2^(bits-1) and every zero is 2^(bits-1), so codes
+ * lie in [1, 2^bits - 1] and the output (scales, zeros, codes, packed words)
+ * feeds lowbit_qgemv and lowbit_qgemm unchanged: (code - zero) * s = q * s.
+ * Arguments, layouts, shape rules, ownership and errors exactly as
+ * lowbit_quantize_rtn.
+ */
+LOWBIT_API int lowbit_quantize_rtn_sym(const void* w_f16, int64_t N, int64_t K, int bits,
+                            int64_t group_size, uint8_t* codes_or_null, uint32_t* packed_or_null,
+                            uint16_t* scales_f16, int32_t* zeros, void* hip_stream);
+
+/*
  * Pack byte codes[N][K] (each < 2^bits; higher bits are ignored) into
  * packed[N][K*bits/32] (the feature request's several-codes-per-word
  * storage; bit order as in the contract above).

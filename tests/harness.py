@@ -28,9 +28,11 @@ def row_chunks(N: int, parts: int):
     return [(r0, min(N, r0 + step)) for r0 in range(0, N, step)]
 
 
-def oracle_quantize(w: np.ndarray, bits: int, group_size: int):
-    """Oracle quantization of all rows (row ranges in parallel threads)."""
+def oracle_quantize(w: np.ndarray, bits: int, group_size: int, symmetric: bool = False):
+    """Oracle quantization of all rows (row ranges in parallel threads): the
+    min-max grid, or the signed symmetric grid when ``symmetric``."""
     N, K = w.shape
+    quantize = oracle.quantize_rtn_sym if symmetric else oracle.quantize_rtn
     G = oracle.groups(K, group_size)
     codes = np.empty((N, K), np.uint8)
     scales = np.empty((N, G), np.float16)
@@ -38,7 +40,7 @@ def oracle_quantize(w: np.ndarray, bits: int, group_size: int):
 
     def run(rng):
         r0, r1 = rng
-        c, s, z = oracle.quantize_rtn(w[r0:r1], bits, group_size)
+        c, s, z = quantize(w[r0:r1], bits, group_size)
         codes[r0:r1], scales[r0:r1], zeros[r0:r1] = c, s, z
 
     with ThreadPoolExecutor(threads()) as ex:

@@ -31,7 +31,7 @@ def declared_entry_points():
 def test_header_declares_the_abi():
     assert declared_entry_points() == sorted(
         ["lowbit_pack", "lowbit_qgemm", "lowbit_qgemv", "lowbit_quantize_rtn",
-         "lowbit_status_string"])
+         "lowbit_quantize_rtn_sym", "lowbit_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lw):
@@ -89,6 +89,14 @@ MIS = P + 4
     (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 4, 0, None, None, P, P, None), "ARG"),
     (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 4, 0, MIS, None, P, P, None), "ARG"),
     (lambda lw: lw.pack_raw(None, 4, 128, 4, P, None), "ARG"),
+    # the symmetric entry point shares the validation
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 128, 1, 0, P, P, P, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 256, 4, 96, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 262144, 2, 0, P, P, P, P, None), "SHAPE"),
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 128, 4, 0, None, None, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 128, 4, 0, P, MIS, P, P, None), "ARG"),
+    (lambda lw: lw.quantize_rtn_sym_raw(None, 0, 128, 4, 0, None, None, None, None, None),
+     "OK"),
     (lambda lw: lw.qgemv_raw(P, 16, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
     (lambda lw: lw.qgemv_raw(P, -1, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
     (lambda lw: lw.qgemv_raw(P, 1, None, P, P, 4, 128, 4, 0, P, None), "ARG"),

@@ -8,7 +8,7 @@ no GPU is present the calls raise.
 
 Functions mirror the C entry points:
 
-  quantize_rtn(w, bits, group_size, codes=True, packed=True) -> dict
+  quantize_rtn(w, bits, group_size, codes=True, packed=True, symmetric=False) -> dict
   pack(codes, bits) -> packed
   qgemv(x, packed, scales, zeros, K, bits, group_size) -> y      (1 <= B <= 15)
   qgemm(x, packed, scales, zeros, K, bits, group_size) -> y      (any B)
@@ -29,7 +29,7 @@ LOWBIT_ERR_HIP = -4
 QGEMV_MAX_B = 15
 QUANTIZE_MAX_K = 131072
 
-EXPORTED = ("lowbit_quantize_rtn", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
+EXPORTED = ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
             "lowbit_status_string")
 
 _lib = None
@@ -52,10 +52,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.lowbit_quantize_rtn.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp, vp, vp]
+    lib.lowbit_quantize_rtn_sym.argtypes = [vp, i64, i64, i32, i64, vp, vp, vp, vp, vp]
     lib.lowbit_pack.argtypes = [vp, i64, i64, i32, vp, vp]
     lib.lowbit_qgemv.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
-    for name in ("lowbit_quantize_rtn", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm"):
+    for name in ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv",
+                 "lowbit_qgemm"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_status_string.restype = ctypes.c_char_p
@@ -114,6 +116,11 @@ def quantize_rtn_raw(w, N, K, bits, group_size, codes, packed, scales, zeros, st
                                               zeros, stream)
 
 
+def quantize_rtn_sym_raw(w, N, K, bits, group_size, codes, packed, scales, zeros, stream) -> int:
+    return load_library().lowbit_quantize_rtn_sym(w, N, K, bits, group_size, codes, packed,
+                                                  scales, zeros, stream)
+
+
 def pack_raw(codes, N, K, bits, packed, stream) -> int:
     return load_library().lowbit_pack(codes, N, K, bits, packed, stream)
 
@@ -132,8 +139,9 @@ def qgemm_raw(x, B, packed, scales, zeros, N, K, bits, group_size, y, stream) ->
 # tensor front end
 # ---------------------------------------------------------------------------
 def quantize_rtn(w, bits: int, group_size: int, codes: bool = True, packed: bool = True,
-                 out: dict | None = None) -> dict:
-    """Min-max RTN quantization of fp16 ``w[N][K]`` on the GPU.
+                 out: dict | None = None, symmetric: bool = False) -> dict:
+    """RTN quantization of fp16 ``w[N][K]`` on the GPU: the min-max grid, or
+    with ``symmetric=True`` the signed symmetric grid (``lowbit_quantize_rtn_sym``).
 
     Returns a dict with ``scales`` (fp16 [N][G]), ``zeros`` (int32 [N][G]) and,
     as requested, ``codes`` (uint8 [N][K]) and ``packed`` (int32 view of the
@@ -153,11 +161,13 @@ def quantize_rtn(w, bits: int, group_size: int, codes: bool = True, packed: bool
         out["codes"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
     if packed and "packed" not in out:
         out["packed"] = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=dev)
-    st = quantize_rtn_raw(w.data_ptr(), N, K, bits, group_size,
-                          _ptr(out.get("codes") if codes else None),
-                          _ptr(out.get("packed") if packed else None),
-                          out["scales"].data_ptr(), out["zeros"].data_ptr(), _stream_handle(dev))
-    _check(st, "lowbit_quantize_rtn")
+    raw, name = ((quantize_rtn_sym_raw, "lowbit_quantize_rtn_sym") if symmetric
+                 else (quantize_rtn_raw, "lowbit_quantize_rtn"))
+    st = raw(w.data_ptr(), N, K, bits, group_size,
+             _ptr(out.get("codes") if codes else None),
+             _ptr(out.get("packed") if packed else None),
+             out["scales"].data_ptr(), out["zeros"].data_ptr(), _stream_handle(dev))
+    _check(st, name)
     return out
 
 

@@ -81,13 +81,9 @@ int check_product(const void* x, int64_t B, const uint32_t* packed, const uint16
   return LOWBIT_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int bits, int64_t group_size,
-                        uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
-                        int32_t* zeros, void* hip_stream) {
+int quantize_checked(const void* w_f16, int64_t N, int64_t K, int bits, int64_t group_size,
+                     bool sym, uint8_t* codes_or_null, uint32_t* packed_or_null,
+                     uint16_t* scales_f16, int32_t* zeros, void* hip_stream) {
   int rc = check_bits(bits);
   if (rc != LOWBIT_OK) return rc;
   rc = check_shape(N, K, bits, group_size);
@@ -101,8 +97,27 @@ int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int bits, int64
       (packed_or_null && !aligned16(packed_or_null)))
     return LOWBIT_ERR_ARG;
   return hip_status(lowbit::launch_quantize(static_cast<const uint16_t*>(w_f16), N, K, bits,
-                                            group_size, codes_or_null, packed_or_null, scales_f16,
-                                            zeros, static_cast<hipStream_t>(hip_stream)));
+                                            group_size, sym, codes_or_null, packed_or_null,
+                                            scales_f16, zeros,
+                                            static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lowbit_quantize_rtn(const void* w_f16, int64_t N, int64_t K, int bits, int64_t group_size,
+                        uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                        int32_t* zeros, void* hip_stream) {
+  return quantize_checked(w_f16, N, K, bits, group_size, false, codes_or_null, packed_or_null,
+                          scales_f16, zeros, hip_stream);
+}
+
+int lowbit_quantize_rtn_sym(const void* w_f16, int64_t N, int64_t K, int bits,
+                            int64_t group_size, uint8_t* codes_or_null, uint32_t* packed_or_null,
+                            uint16_t* scales_f16, int32_t* zeros, void* hip_stream) {
+  return quantize_checked(w_f16, N, K, bits, group_size, true, codes_or_null, packed_or_null,
+                          scales_f16, zeros, hip_stream);
 }
 
 int lowbit_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,

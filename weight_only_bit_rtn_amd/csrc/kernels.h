@@ -8,9 +8,10 @@ namespace lowbit {
 
 size_t quantize_lds_bytes(int64_t K, int64_t G);
 
+// Min-max grid (sym = false) or signed symmetric grid (sym = true).
 hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
-                           uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
-                           hipStream_t stream);
+                           bool sym, uint8_t* codes, uint32_t* packed, uint16_t* scales,
+                           int32_t* zeros, hipStream_t stream);
 
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
                        hipStream_t stream);

@@ -124,20 +124,31 @@ struct Params {
   uint32_t zz;       // z - kRoundBits (mod 2^32): folds the rounding offset into the zero
   uint32_t s16;      // stored scale (fp16 bits)
   int z;             // stored zero point
+  int qlo;           // lowest code: 0 (min-max grid) or 1 (signed symmetric grid)
 };
 
-// scale = fp16((max - min) / M), a zero scale replaced by 1, zero =
-// rint(-min / scale); every quotient equal to the correctly rounded fp32 one.
+// The fp32 quotient x / D for a small constant divisor D, correctly rounded
+// (the two-term reciprocal form, checked for every fp32 significand and
+// D = 3, 7, 15; D = 1 is exact).
+template <int D>
+__device__ __forceinline__ float div_const(float x) {
+  constexpr float m_hi = 1.0f / (float)D;
+  constexpr float m_lo = (float)((1.0 - (double)D * (double)m_hi) * (double)m_hi);
+  return __builtin_fmaf(x, m_hi, x * m_lo);
+}
+
+// Min-max grid: scale = fp16((max - min) / M), zero = rint(-min / scale).
+// Signed symmetric grid (SYM): scale = fp16(max|w| / qmax), qmax =
+// 2^(b-1) - 1, zero = 2^(b-1), codes from 1.  A zero scale becomes 1.  Every
+// quotient equals the correctly rounded fp32 one.
 template <int BITS>
-__device__ __forceinline__ Params group_params(uint32_t ext) {
-  constexpr float M = (float)((1 << BITS) - 1);
-  constexpr float m_hi = 1.0f / M;
-  constexpr float m_lo = (float)((1.0 - (double)M * (double)m_hi) * (double)m_hi);
+__device__ __forceinline__ Params group_params(uint32_t ext, bool sym) {
+  constexpr int M = (1 << BITS) - 1;
+  constexpr int QMAX = (1 << (BITS - 1)) - 1;
   const h2_t e = as_h2(ext);
   const float lo = (float)e.x;
   const float hi = -(float)e.y;
-  const float d = hi - lo;
-  float s32 = __builtin_fmaf(d, m_hi, d * m_lo);
+  float s32 = sym ? div_const<QMAX>(fmaxf(-lo, hi)) : div_const<M>(hi - lo);
   // The scale is rounded twice: to fp32 (the quotient), then to fp16.  This
   // empty barrier keeps the fp32 value: otherwise the fma and the conversion
   // are folded into one mixed-precision fma that rounds once, straight to
@@ -150,13 +161,14 @@ __device__ __forceinline__ Params group_params(uint32_t ext) {
   p.r_hi = 1.0f / s;
   p.r_lo = __builtin_fmaf(-s, p.r_hi, 1.0f) * p.r_hi;
   const float nl = -lo;
-  p.z = (int)__builtin_rintf(__builtin_fmaf(nl, p.r_hi, nl * p.r_lo));
+  p.z = sym ? 1 << (BITS - 1) : (int)__builtin_rintf(__builtin_fmaf(nl, p.r_hi, nl * p.r_lo));
   p.zz = (uint32_t)p.z - kRoundBits;
   p.s16 = s16;
+  p.qlo = sym ? 1 : 0;
   return p;
 }
 
-// q = clamp(rint(w / s) + z, 0, M) for one fp16 weight.
+// q = clamp(rint(w / s) + z, qlo, M) for one fp16 weight.
 template <int BITS>
 __device__ __forceinline__ uint32_t code_of(_Float16 wh, const Params& p) {
   constexpr int M = (1 << BITS) - 1;
@@ -165,7 +177,7 @@ __device__ __forceinline__ uint32_t code_of(_Float16 wh, const Params& p) {
   // fp16 weight directly (the sign of a zero product cannot change the code)
   const float v = __builtin_fmaf(w, p.r_hi, __builtin_fmaf(w, p.r_lo, 0.0f));
   const uint32_t t = __builtin_bit_cast(uint32_t, v + kRoundMagic) + p.zz;
-  return (uint32_t)min(max((int)t, 0), M);
+  return (uint32_t)min(max((int)t, p.qlo), M);
 }
 
 // The 8 codes of a chunk, packed least significant first.
@@ -238,7 +250,7 @@ __device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t prs, uint32_t
 template <int BITS, int NL, int MODE, bool CODES>
 __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
     const uint16_t* __restrict__ w, int K, int G, int cpg /* chunks per group */,
-    int lg_cpg /* log2(cpg) when MODE == kLaneGroups */, uint8_t* __restrict__ codes,
+    int lg_cpg /* log2(cpg) when MODE == kLaneGroups */, int sym, uint8_t* __restrict__ codes,
     uint32_t* __restrict__ packed, uint16_t* __restrict__ scales, int32_t* __restrict__ zeros) {
   extern __shared__ uint32_t ent[];  // kLdsGroups: one (min, -max) pair per chunk
 
@@ -295,7 +307,7 @@ __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
       ext = wave_ext[0];
       for (int k = 1; k < waves; ++k) ext = pk_min(ext, wave_ext[k]);
     }
-    const Params p = group_params<BITS>(ext);
+    const Params p = group_params<BITS>(ext, sym != 0);
     if (t == 0) {
       scales[row] = (uint16_t)p.s16;
       zeros[row] = p.z;
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
       if (cpg >= 64)
         ext = pk_min((uint32_t)__builtin_amdgcn_readlane((int)ext, 0),
                      (uint32_t)__builtin_amdgcn_readlane((int)ext, 32));
-      const Params p = group_params<BITS>(ext);
+      const Params p = group_params<BITS>(ext, sym != 0);
       if ((lane & (cpg - 1)) == 0 && c < C) {
         const int64_t j = row * G + (c >> lg_cpg);
         scales[j] = (uint16_t)p.s16;
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
       uint32_t ext = kPosInfPair;
       for (int e = lane; e < cpg; e += kWave) ext = pk_min(ext, ent[j * cpg + e]);
       ext = reduce_wave(ext);
-      const Params p = group_params<BITS>(ext);
+      const Params p = group_params<BITS>(ext, sym != 0);
       if (lane == 0) {
         scales[row * G + j] = (uint16_t)p.s16;
         zeros[row * G + j] = p.z;
@@ -350,6 +362,7 @@ __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
       p.r_hi = __builtin_bit_cast(float, ent[j * cpg]);
       p.r_lo = __builtin_bit_cast(float, ent[j * cpg + 1]);
       p.zz = ent[j * cpg + 2];
+      p.qlo = sym ? 1 : 0;
       emit(i, p);
     }
   }
@@ -387,17 +400,17 @@ constexpr int kChunkCounts[] = {1, 2, 4, 6, 8, 16};
 
 template <int BITS, int MODE>
 hipError_t launch_mode(const uint16_t* w, int64_t N, int K, int G, int cpg, int lg_cpg, int T,
-                       int nl, size_t lds, uint8_t* codes, uint32_t* packed, uint16_t* scales,
-                       int32_t* zeros, hipStream_t stream) {
+                       int nl, size_t lds, int sym, uint8_t* codes, uint32_t* packed,
+                       uint16_t* scales, int32_t* zeros, hipStream_t stream) {
   const dim3 grid((unsigned)N), block((unsigned)T);
 #define LOWBIT_Q_NL(n)                                                                      \
   case n:                                                                                   \
     if (codes)                                                                              \
       hipLaunchKernelGGL((rtn_quantize_kernel<BITS, n, MODE, true>), grid, block, lds, stream, \
-                         w, K, G, cpg, lg_cpg, codes, packed, scales, zeros);               \
+                         w, K, G, cpg, lg_cpg, sym, codes, packed, scales, zeros);               \
     else                                                                                    \
       hipLaunchKernelGGL((rtn_quantize_kernel<BITS, n, MODE, false>), grid, block, lds,       \
-                         stream, w, K, G, cpg, lg_cpg, codes, packed, scales, zeros);       \
+                         stream, w, K, G, cpg, lg_cpg, sym, codes, packed, scales, zeros);       \
     break;
   switch (nl) {
     LOWBIT_Q_NL(1)
@@ -415,28 +428,28 @@ hipError_t launch_mode(const uint16_t* w, int64_t N, int K, int G, int cpg, int 
 
 template <int BITS>
 hipError_t launch_bits(const uint16_t* w, int64_t N, int K, int G, int cpg, int T, int nl,
-                       uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
-                       hipStream_t stream) {
+                       int sym, uint8_t* codes, uint32_t* packed, uint16_t* scales,
+                       int32_t* zeros, hipStream_t stream) {
   const bool pow2 = (cpg & (cpg - 1)) == 0;
   if (G == 1)
-    return launch_mode<BITS, kRowGroup>(w, N, K, G, cpg, 0, T, nl, 0, codes, packed, scales,
-                                        zeros, stream);
+    return launch_mode<BITS, kRowGroup>(w, N, K, G, cpg, 0, T, nl, 0, sym, codes, packed,
+                                        scales, zeros, stream);
   if (pow2 && cpg <= kWave) {
     int lg = 0;
     while ((1 << lg) < cpg) ++lg;
-    return launch_mode<BITS, kLaneGroups>(w, N, K, G, cpg, lg, T, nl, 0, codes, packed, scales,
-                                          zeros, stream);
+    return launch_mode<BITS, kLaneGroups>(w, N, K, G, cpg, lg, T, nl, 0, sym, codes, packed,
+                                          scales, zeros, stream);
   }
   const size_t lds = (size_t)(K / 8) * 4;
-  return launch_mode<BITS, kLdsGroups>(w, N, K, G, cpg, 0, T, nl, lds, codes, packed, scales,
-                                       zeros, stream);
+  return launch_mode<BITS, kLdsGroups>(w, N, K, G, cpg, 0, T, nl, lds, sym, codes, packed,
+                                       scales, zeros, stream);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t gsz,
-                           uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
-                           hipStream_t stream) {
+                           bool sym, uint8_t* codes, uint32_t* packed, uint16_t* scales,
+                           int32_t* zeros, hipStream_t stream) {
   const int64_t g = gsz == 0 ? K : gsz;
   const int G = (int)(K / g);
   const int cpg = (int)(g / 8);
@@ -455,11 +468,14 @@ hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, in
   if (nl == 0) return hipErrorInvalidValue;
   switch (bits) {
     case 2:
-      return launch_bits<2>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
+      return launch_bits<2>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
+                            stream);
     case 3:
-      return launch_bits<3>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
+      return launch_bits<3>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
+                            stream);
     default:
-      return launch_bits<4>(w, N, (int)K, G, cpg, T, nl, codes, packed, scales, zeros, stream);
+      return launch_bits<4>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
+                            stream);
   }
 }
 
