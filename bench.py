@@ -14,9 +14,11 @@ value = algorithmic bytes of the step (packed words + scales + zeros + x + y)
 over the wall time of the timed steps; roofline.achieved = the same bytes per
 GEMV launch over the average launch duration, from HIP events recorded on the
 launch stream around the timed region (elapsed / launches).  The quantizer
-(lowbit_quantize_rtn) and the matrix-core product (lowbit_qgemm, Llama-70B MLP
-shape at batch 16/32/64) are measured in the same run as separate stages.  The CPU baseline times the C oracle's
-dequantize + fp64 product on a sample of rows of the same layers.
+(lowbit_quantize_rtn, and lowbit_quantize_rtn_sym for the signed symmetric
+grid), every workload's products and the matrix-core product (lowbit_qgemm,
+Llama-70B MLP shape at batch 16/32/64) are measured in the same run as
+separate stages.  The CPU baseline times the C oracle's dequantize + fp64
+product on a sample of rows of the same layers.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
                        [--no-stages] [--only-gemv]
@@ -121,31 +123,37 @@ def time_launches(torch, fn, count: int, spread: bool = False):
 def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     import synth
     stages = {}
-    # quantize + pack of the OPT-175B 3-bit layers (reads 2 B per weight)
-    for layer in synth.WORKLOADS["opt175b_3bit"]:
+    # quantize + pack (reads 2 B per weight): the OPT-175B 3-bit per-row
+    # layers and the Llama-70B 4-bit layer (groups of 128), on the min-max
+    # grid and, for the larger two, on the signed symmetric grid
+    runs = [(synth.WORKLOADS["opt175b_3bit"][0], False), (synth.WORKLOADS["opt175b_3bit"][1], False),
+            (synth.WORKLOADS["opt175b_3bit"][1], True), (synth.WORKLOADS["llama70b_mlp_4bit"][0], False),
+            (synth.WORKLOADS["llama70b_mlp_4bit"][0], True)]
+    for layer, sym in runs:
         dev = torch.device("cuda:0")
         w = torch.from_numpy(layer.weights()).to(dev)
-        G = 1
+        G = 1 if layer.group_size == 0 else layer.K // layer.group_size
         packed = torch.empty((layer.N, layer.K * layer.bits // 32), dtype=torch.int32, device=dev)
         scales = torch.empty((layer.N, G), dtype=torch.float16, device=dev)
         zeros = torch.empty((layer.N, G), dtype=torch.int32, device=dev)
+        raw = lw.quantize_rtn_sym_raw if sym else lw.quantize_rtn_raw
 
         def q(_):
-            st = lw.quantize_rtn_raw(w.data_ptr(), layer.N, layer.K, layer.bits, layer.group_size,
-                                     None, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                                     stream)
+            st = raw(w.data_ptr(), layer.N, layer.K, layer.bits, layer.group_size, None,
+                     packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(), stream)
             if st != 0:
                 raise RuntimeError(lw.status_string(st))
 
         q(0)
         avg, med, p10, p90 = time_launches(torch, q, reps, spread=True)
         nbytes = quantize_bytes(layer.N, layer.K, layer.bits, layer.group_size)
-        stages[f"quantize_pack/{layer.name}"] = {
+        stages[f"{'quantize_pack_sym' if sym else 'quantize_pack'}/{layer.name}"] = {
             "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2),
             "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2), "bytes": nbytes,
             "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
         del w, packed, scales, zeros
+        torch.cuda.empty_cache()
     # every workload's products
     for name, layers in synth.WORKLOADS.items():
         for layer in layers:
