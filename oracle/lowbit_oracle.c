@@ -101,7 +101,12 @@ uint16_t orc_f64_to_f16(double v) {
     return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
 }
 
-static int valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4; }
+/* Widths: 2, 3 and 4 bits (the feature request's packed widths), and 8
+ * bits (reading R15: BladeLLM's weight-only mode supports 8 and 4 bits,
+ * "Quantization modes"; GGUF lists 8-bit round-to-nearest block types next to
+ * the 4-bit ones).  Every formula below is written for any b; at 8 bits the
+ * bitstream of R5 puts code k in byte k of the row. */
+static int valid_bits(int bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
 
 /* group_size 0 means one group per row */
 static int64_t groups_of(int64_t K, int64_t group_size) {

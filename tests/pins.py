@@ -131,7 +131,7 @@ def check_pack_closed_forms(o) -> None:
 def check_pack_bigint(o) -> None:
     """Packing against a Python big-integer bitstream, plus the round trip."""
     rng = np.random.default_rng(7)
-    for bits in (2, 3, 4):
+    for bits in (2, 3, 4, 8):
         for K in (32, 64, 96, 128, 160, 416):
             if (K * bits) % 32:
                 continue
@@ -167,7 +167,7 @@ def check_invariants(o) -> None:
     for label, w in _random_weight_sets(rng):
         N, K = w.shape
         wf = w.astype(np.float64)
-        for bits in (2, 3, 4):
+        for bits in (2, 3, 4, 8):
             M = (1 << bits) - 1
             for g in (0, 32, 64, 128):
                 codes, scales, zeros = o.quantize_rtn(w, bits, g)
@@ -203,7 +203,7 @@ def check_scale_is_nearest(o) -> None:
     """
     rng = np.random.default_rng(99)
     for label, w in _random_weight_sets(rng):
-        for bits in (2, 3, 4):
+        for bits in (2, 3, 4, 8):
             M = (1 << bits) - 1
             for g in (0, 64):
                 _, scales, _ = o.quantize_rtn(w, bits, g)
@@ -224,7 +224,7 @@ def check_dequant_is_nearest(o) -> None:
     """deq is the fp16 nearest to the exact rational (q - zero) * scale."""
     rng = np.random.default_rng(5)
     for label, w in _random_weight_sets(rng):
-        for bits in (2, 4):
+        for bits in (2, 4, 8):
             codes, scales, zeros = o.quantize_rtn(w, bits, 32)
             deq = o.dequant(codes, scales, zeros, bits, 32).view(np.uint16)
             for n in range(0, w.shape[0], 4):
@@ -250,10 +250,10 @@ def _rint_by_search(t: Fraction) -> int:
 
 def check_rtn_bruteforce(o) -> None:
     rng = np.random.default_rng(31337)
-    for trial in range(60):
-        bits = (2, 3, 4)[trial % 3]
+    for trial in range(80):
+        bits = (2, 3, 4, 8)[trial % 4]
         M = (1 << bits) - 1
-        g = (0, 2, 4)[(trial // 3) % 3]
+        g = (0, 2, 4)[(trial // 4) % 3]
         w = (rng.standard_normal((4, 8)) * rng.choice([0.02, 1.0, 40.0])).astype(np.float16)
         if trial % 7 == 0:
             w[1, :4] = w[1, 0]                         # a constant group
@@ -306,7 +306,7 @@ def check_sym_invariants(o) -> None:
     for label, w in _random_weight_sets(rng):
         N, K = w.shape
         wf = w.astype(np.float64)
-        for bits in (2, 3, 4):
+        for bits in (2, 3, 4, 8):
             M, z, qmax = (1 << bits) - 1, 1 << (bits - 1), (1 << (bits - 1)) - 1
             for g in (0, 32, 128):
                 codes, scales, zeros = o.quantize_rtn_sym(w, bits, g)
@@ -339,7 +339,7 @@ def check_sym_scale_is_nearest(o) -> None:
     a zero result is stored as 1.0."""
     rng = np.random.default_rng(606)
     for label, w in _random_weight_sets(rng):
-        for bits in (2, 3, 4):
+        for bits in (2, 3, 4, 8):
             qmax = (1 << (bits - 1)) - 1
             for g in (0, 64):
                 _, scales, _ = o.quantize_rtn_sym(w, bits, g)
@@ -360,10 +360,10 @@ def check_sym_bruteforce(o) -> None:
     """Every code, less the zero point, is the grid level of [-qmax, qmax]
     nearest the fp32 quotient w / s (ties to the even level)."""
     rng = np.random.default_rng(8080)
-    for trial in range(45):
-        bits = (2, 3, 4)[trial % 3]
+    for trial in range(60):
+        bits = (2, 3, 4, 8)[trial % 4]
         z, qmax = 1 << (bits - 1), (1 << (bits - 1)) - 1
-        g = (0, 2, 4)[(trial // 3) % 3]
+        g = (0, 2, 4)[(trial // 4) % 3]
         w = (rng.standard_normal((4, 8)) * rng.choice([0.02, 1.0, 40.0])).astype(np.float16)
         if trial % 5 == 0:
             w[2, :4] = 0
