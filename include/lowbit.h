@@ -15,6 +15,9 @@
  *  - Several codes share one machine word ([Feature Request] 4bit and 2bit
  *    and 1bit quantization support: two 4-bit codes per byte, four 2-bit
  *    codes per uint8, sixteen 2-bit codes per int32).
+ *  - Widths b = 2, 3, 4 and 8 (8 and 4 bits are BladeLLM's weight-only
+ *    widths, "Quantization modes"; GGUF has 8-bit round-to-nearest block
+ *    types beside the 4-bit ones).
  *  - The low-bit weights stay in GPU memory and are turned back into fp16 by
  *    the GPU's own cores inside the matrix product (same feature request;
  *    "weight_only_quant" in BladeLLM model quantization, "Quantization modes",
@@ -28,8 +31,8 @@
  *  - q = clamp((int) rint(fl32(w / s)) + zero, 0, M); divisions are IEEE
  *    fp32 divisions, rint rounds half to even.
  *  - Packing: per row, code k occupies bits [bits*k, bits*k + bits) of a
- *    little-endian stream of 32-bit words; 3-bit codes straddle words; every
- *    row starts on a word boundary.
+ *    little-endian stream of 32-bit words; 3-bit codes straddle words; 8-bit
+ *    code k is byte k of the row; every row starts on a word boundary.
  *  - deq(q) = fp16_rne((q - zero) * s), the product exact before one
  *    rounding;  y[b][n] = fp16_rne( sum_k x[b][k] * deq[n][k] ), accumulated
  *    in fp32 (summation order unspecified).
@@ -77,7 +80,7 @@ extern "C" {
 #define LOWBIT_OK 0
 #define LOWBIT_ERR_ARG (-1)         /* null / misaligned pointer, negative size, B out of range */
 #define LOWBIT_ERR_SHAPE (-2)       /* K or group_size break the shape rules */
-#define LOWBIT_ERR_UNSUPPORTED (-3) /* bits not in {2, 3, 4} */
+#define LOWBIT_ERR_UNSUPPORTED (-3) /* bits not in {2, 3, 4, 8} */
 #define LOWBIT_ERR_HIP (-4)         /* the HIP runtime refused a launch or query */
 
 #define LOWBIT_QUANTIZE_MAX_K 131072

@@ -3,7 +3,8 @@
  *      r_lo = fl32(fma(-s, r_hi, 1) * r_hi), for every finite fp16 w and every
  *      STEP-th positive finite fp16 s (STEP = 1 is the exhaustive check);
  *  (2) fl32(d / M) == fma(d, m_hi, fl32(d * m_lo)) for every fp32 significand d
- *      and M = 3, 7, 15;
+ *      and M = 3, 7, 15, 127, 255 (the min-max divisors 2^b - 1 and the
+ *      symmetric divisors 2^(b-1) - 1 of b = 2, 3, 4, 8);
  *  (3) |w| / s < 2^22 for groups whose extrema lie within 8 fp16 steps of
  *      each other (where |w| / s is largest), so v + 1.5 * 2^23 rounds exactly.
  * Prints one line per check and exits non-zero on any failure. */
@@ -51,8 +52,8 @@ int main(int argc, char** argv) {
   }
   printf("quotient identity: %ld pairs, %ld mismatches\n", n, bad);
   long bad2 = 0;
-  const int Ms[3] = {3, 7, 15};
-  for (int i = 0; i < 3; ++i) {
+  const int Ms[5] = {3, 7, 15, 127, 255};
+  for (int i = 0; i < 5; ++i) {
     volatile float mv = (float)Ms[i];
     const float m = mv, m_hi = 1.0f / m, m_lo = fmaf(-m, m_hi, 1.0f) * m_hi;
     for (uint32_t f = 0; f < (1u << 23); ++f) {
@@ -65,7 +66,7 @@ int main(int argc, char** argv) {
   }
   printf("scale identity: %ld mismatches\n", bad2);
   double worst = 0;
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 5; ++i) {
     for (uint32_t lb = 0; lb < 0x10000; ++lb) {
       if (((lb >> 10) & 31) == 31) continue;
       const float lo = h2f((uint16_t)lb);

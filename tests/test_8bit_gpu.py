@@ -1,0 +1,200 @@
+"""8-bit codes on the GPU against the oracle: quantization on both grids
+(min-max and signed symmetric), packing, and both products, through the C ABI.
+
+Bars: scales, zeros, codes and packed words bit-exact; y within
+|y - y_ref| <= 1e-3 |y_ref| + 1e-4 per element (stress inputs add the fp32
+summation allowance of harness.assert_y_close).  Shapes span several tiles
+with ragged tails; group sizes reach every scale/zero layout of the products
+(one per row, power-of-two groups, other groups, groups spanning a lane's
+units); the degenerate kinds reach the exact per-code decode (zero points
+outside the code range, scales of 256 and more) and subnormal scales.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import harness
+import synth
+
+pytestmark = pytest.mark.gpu
+
+BITS = 8
+
+
+@pytest.fixture(scope="module")
+def lw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_bit_rtn_amd as lw
+    lw.load_library()
+    return lw
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _to_gpu(a):
+    import torch
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _weights(kind: str, N: int, K: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    if kind == "mixed":          # tiny, normal, constant and zero rows
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        w[::3] *= 1e-3
+        w[1::5] = 0.37
+        w[2::7] = 0.0
+        return w.astype(np.float16)
+    if kind == "tiny":           # subnormal scales
+        return (rng.standard_normal((N, K)) * 3e-5).astype(np.float16)
+    if kind == "offset":         # one-signed groups: zero points outside [0, 255]
+        return (100 + 0.1 * rng.standard_normal((N, K))).astype(np.float16)
+    if kind == "huge":           # ranges near the fp16 limit: scales >= 256
+        return rng.uniform(-40000, 40000, (N, K)).astype(np.float16)
+    if kind == "wide":
+        return (rng.standard_normal((N, K)) * 30).astype(np.float16)
+    raise ValueError(kind)
+
+
+def _check_quantize(lw, w, g, symmetric, what, codes_too=(True, False)):
+    codes, scales, zeros, packed = harness.oracle_quantize(w, BITS, g, symmetric=symmetric)
+    for want_codes in codes_too:
+        out = lw.quantize_rtn(_to_gpu(w), BITS, g, codes=want_codes, packed=True,
+                              symmetric=symmetric)
+        res = {k: v.cpu().numpy() for k, v in out.items()}
+        bad = np.argwhere(res["scales"].view(np.uint16) != scales.view(np.uint16))
+        assert bad.size == 0, f"{what}: scales differ at {bad[:5].tolist()}"
+        assert np.array_equal(res["zeros"], zeros), f"{what}: zeros"
+        if want_codes:
+            bad = np.argwhere(res["codes"] != codes)
+            assert bad.size == 0, f"{what}: codes differ at {bad[:5].tolist()}"
+        bad = np.argwhere(res["packed"].view(np.uint32) != packed)
+        assert bad.size == 0, f"{what}: packed words differ at {bad[:5].tolist()}"
+    return codes, scales, zeros, packed
+
+
+QUANT_CASES = [(1, 32, 0), (5, 96, 32), (17, 2080, 0), (17, 2080, 32), (67, 4128, 96),
+               (67, 4096, 128), (6, 4096, 256), (3, 8192, 1024), (7, 12320, 160),
+               (2, 98304, 96), (3, 65600, 0), (2, 131072, 0), (2, 131072, 64),
+               (2, 131072, 16384)]
+
+
+@pytest.mark.parametrize("N,K,g", QUANT_CASES)
+@pytest.mark.parametrize("symmetric", [False, True], ids=["minmax", "sym"])
+def test_quantize_8bit(lw, N, K, g, symmetric):
+    _say(f"[8-bit quantize] N={N} K={K} g={g} sym={symmetric}")
+    w = _weights("mixed", N, K, seed=N + K + g)
+    _check_quantize(lw, w, g, symmetric, f"8-bit N={N} K={K} g={g} sym={symmetric}")
+
+
+@pytest.mark.parametrize("kind", ["tiny", "offset", "huge", "wide"])
+@pytest.mark.parametrize("symmetric", [False, True], ids=["minmax", "sym"])
+def test_quantize_8bit_degenerate(lw, kind, symmetric):
+    for g in (0, 32, 96):
+        _check_quantize(lw, _weights(kind, 9, 384, seed=3), g, symmetric,
+                        f"8-bit {kind} g={g} sym={symmetric}")
+
+
+def test_quantize_8bit_ties(lw):
+    """Weights on the half-way points of a unit grid: rint takes the even
+    neighbour, and the top of the range clamps."""
+    row = np.concatenate([np.arange(0, 255, dtype=np.float32) + 0.5, [0.0, 255.0]])
+    w = np.resize(row, (3, 512)).astype(np.float16)
+    w[1] = -w[1]
+    _check_quantize(lw, w, 0, False, "8-bit ties minmax")
+    _check_quantize(lw, w, 256, True, "8-bit ties sym")
+
+
+def test_pack_8bit(lw):
+    import torch
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 256, (37, 4128), dtype=np.uint8)
+    want = harness.oracle.pack(codes, BITS)
+    got = lw.pack(_to_gpu(codes), BITS)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), want)
+    # code k is byte k of the row
+    assert np.array_equal(want.view(np.uint8).reshape(codes.shape), codes)
+
+
+def _check_products(lw, w, g, batches, kernel, symmetric=False, stress=False, what="",
+                    x_std=1.0):
+    import torch
+    N, K = w.shape
+    codes, scales, zeros, packed = harness.oracle_quantize(w, BITS, g, symmetric=symmetric)
+    args = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, BITS, g]
+    for B in batches:
+        x = synth.normal_f16(B, K, x_std, seed=B + 9, stream=2)
+        y = getattr(lw, kernel)(_to_gpu(x), *args)
+        torch.cuda.synchronize()
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, BITS, g)
+        terms = harness.oracle_abs_y(x, packed, scales, zeros, K, BITS, g) if stress else None
+        harness.assert_y_close(y.cpu().numpy(), y_ref,
+                               f"8-bit {kernel} {what} N={N} K={K} g={g} B={B}", terms, K)
+
+
+PRODUCT_CASES = [(1, 32, 0), (5, 96, 32), (33, 640, 128), (17, 1280, 256), (40, 2176, 128),
+                 (67, 4128, 0), (67, 4128, 96), (70, 4224, 64), (19, 8320, 0), (21, 8192, 1024)]
+
+
+@pytest.mark.parametrize("N,K,g", PRODUCT_CASES)
+def test_qgemv_8bit(lw, N, K, g):
+    _say(f"[8-bit qgemv] N={N} K={K} g={g}")
+    w = _weights("normal", N, K, seed=N + 3 * K)
+    _check_products(lw, w, g, [1, 2, 3, 5, 8, 9, 15], "qgemv")
+
+
+@pytest.mark.parametrize("N,K,g", PRODUCT_CASES)
+def test_qgemm_8bit(lw, N, K, g):
+    _say(f"[8-bit qgemm] N={N} K={K} g={g}")
+    w = _weights("normal", N, K, seed=N + 5 * K)
+    _check_products(lw, w, g, [1, 16, 17, 33, 64, 70], "qgemm")
+
+
+@pytest.mark.parametrize("kind", ["mixed", "tiny", "offset", "huge", "wide"])
+def test_products_8bit_degenerate(lw, kind):
+    _say(f"[8-bit degenerate products] {kind}")
+    w = _weights(kind, 70, 4160, seed=17)
+    stress = kind in ("offset", "huge", "wide")
+    # weights near 4e4 against N(0, 1e-3) activations keep y inside fp16
+    x_std = 1e-3 if kind == "huge" else 1.0
+    for g in (0, 64, 320):
+        for symmetric in (False, True):
+            _check_products(lw, w, g, [1, 4], "qgemv", symmetric, stress, kind, x_std)
+            _check_products(lw, w, g, [16, 40], "qgemm", symmetric, stress, kind, x_std)
+
+
+# Two workload shapes at 8 bits, full size: every code bit-exact, products on
+# sampled rows, in the launch configurations the other widths use.
+FULL = [synth.Layer("opt175b_attn_12288_8bit", 12288, 12288, 8, 0, (1,)),
+        synth.Layer("llama70b_up_28672x8192_8bit", 28672, 8192, 8, 128, (1, 16, 64))]
+
+
+@pytest.mark.parametrize("layer", FULL, ids=lambda L: L.name)
+def test_8bit_full_size(lw, layer):
+    import torch
+    _say(f"[8-bit full size] {layer.name}")
+    w = layer.weights()
+    codes, scales, zeros, packed = _check_quantize(lw, w, layer.group_size, False, layer.name,
+                                                   (False,))
+    rows = harness.sample_rows(layer.N)
+    K, g = layer.K, layer.group_size
+    args = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, BITS, g]
+    for B in layer.batches:
+        x = layer.activations(B)
+        kernel = "qgemv" if B < 16 else "qgemm"
+        y = getattr(lw, kernel)(_to_gpu(x), *args)
+        torch.cuda.synchronize()
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, BITS, g, rows=rows)
+        harness.assert_y_close(y.cpu().numpy()[:, rows], y_ref, f"{layer.name} B={B}")

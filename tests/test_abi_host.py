@@ -70,7 +70,9 @@ MIS = P + 4
     # bit width
     (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 5, 0, P, P, P, P, None), "UNSUPPORTED"),
     (lambda lw: lw.pack_raw(P, 4, 128, 1, P, None), "UNSUPPORTED"),
-    (lambda lw: lw.qgemv_raw(P, 1, P, P, P, 4, 128, 8, 0, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.qgemv_raw(P, 1, P, P, P, 4, 128, 6, 0, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 7, 0, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.quantize_rtn_sym_raw(P, 4, 128, 5, 0, P, P, P, P, None), "UNSUPPORTED"),
     (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 0, 0, P, None), "UNSUPPORTED"),
     # shapes
     (lambda lw: lw.quantize_rtn_raw(P, 4, 0, 4, 0, P, P, P, P, None), "SHAPE"),

@@ -1,4 +1,4 @@
-"""Python binding of liblowbit (weight-only 2/3/4-bit RTN linear layers, gfx950).
+"""Python binding of liblowbit (weight-only 2/3/4/8-bit RTN linear layers, gfx950).
 
 Argument marshalling only: every step of quantization, packing and the
 dequantize-and-multiply products runs in the HIP kernels of ``liblowbit.so``,

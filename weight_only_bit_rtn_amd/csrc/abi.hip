@@ -51,7 +51,7 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_bits(int bits) {
-  return (bits == 2 || bits == 3 || bits == 4) ? LOWBIT_OK : LOWBIT_ERR_UNSUPPORTED;
+  return (bits == 2 || bits == 3 || bits == 4 || bits == 8) ? LOWBIT_OK : LOWBIT_ERR_UNSUPPORTED;
 }
 
 int check_shape(int64_t N, int64_t K, int bits, int64_t group_size) {
@@ -168,7 +168,7 @@ const char* lowbit_status_string(int status) {
       return "unsupported shape (K must be a positive multiple of 32 with K*bits a multiple of "
              "128; group_size 0 or a multiple of 32 dividing K)";
     case LOWBIT_ERR_UNSUPPORTED:
-      return "unsupported bit width (2, 3 or 4)";
+      return "unsupported bit width (2, 3, 4 or 8)";
     case LOWBIT_ERR_HIP:
       return "HIP runtime error while launching";
     default:

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
           b.w[u][4] = vb.y;
           b.w[u][5] = vb.z;
         } else {
-          const int gu = min(ur.ka >> (BITS == 4 ? 5 : 6), units_per_row - 1);
+          const int gu = min(ur.ka / U::CODES, units_per_row - 1);
           const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + 16u * gu, 0, 2);
           b.w[u][0] = v.x;
           b.w[u][1] = v.y;
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     // rows of one 512-k step), issuing the same loads every step; halves past
     // K or past B read zeros (their offset lies outside the buffer
     // descriptor).  One wave instruction covers the 64 (unit, quad) entries of
-    // one batch row, so its loads read that row's x contiguously; 4-bit
-    // entries are eight consecutive k (one 16-byte load), 2- and 3-bit
+    // one batch row, so its loads read that row's x contiguously; 4- and
+    // 8-bit entries are eight consecutive k (one 16-byte load), 2- and 3-bit
     // entries two runs of four (two 8-byte loads).  In LDS, entry (m = unit
     // slot * Q + quad, batch tile, lane group h, batch row i16) sits at
     // (m * BT + bt) * 64 + 16 h + (i16 ^ (m & 15)): the swizzle spreads one
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const uint32_t ol = xk[i][0] + tk < K ? xo[i][0] + tb : 0xFFFFFFF0u;
-        if constexpr (BITS == 4) {
+        if constexpr (BITS == 4 || BITS == 8) {
           const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, ol, 0, 0);
           xr[i] = make_uint4(v.x, v.y, v.z, v.w);
         } else {
@@ -278,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
       uint4* xs = lds + buf * XBUF;
 #pragma unroll
       for (int i = 0; i < E; ++i)
-        xs[xl[i]] = make_uint4(__builtin_amdgcn_perm(xr[i].z, xr[i].x, 0x05040100u),
+        xs[xl[i]] = BITS == 8 ? xr[i]  // 8-bit slots pair neighbouring codes: x as loaded
+                              : make_uint4(__builtin_amdgcn_perm(xr[i].z, xr[i].x, 0x05040100u),
                                __builtin_amdgcn_perm(xr[i].z, xr[i].x, 0x07060302u),
                                __builtin_amdgcn_perm(xr[i].w, xr[i].y, 0x05040100u),
                                __builtin_amdgcn_perm(xr[i].w, xr[i].y, 0x07060302u));
@@ -500,7 +501,8 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
   // wide groups: a lane's units of one step (at most 4 x 32 codes at 4 bits,
-  // 2 x 64 at 2 bits, starting on a multiple of that span) lie in one group
+  // 2 x 64 at 2 bits, 8 x 16 at 8 bits, starting on a multiple of that span)
+  // lie in one group
   const bool wide = bits != 3 && gshift >= 0 && gsz >= 128;
   const int gm = G == 1 ? kPerRow : wide ? kWideGroups : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
@@ -524,6 +526,8 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
       LOWBIT_QGEMM_GM(2)
     case 3:
       LOWBIT_QGEMM_GM(3)
+    case 8:
+      LOWBIT_QGEMM_GM(8)
     default:
       LOWBIT_QGEMM_GM(4)
   }

@@ -29,6 +29,8 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
       return launch_qgemv_bits<2>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
     case 3:
       return launch_qgemv_bits<3>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+    case 8:
+      return launch_qgemv_bits<8>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
     default:
       return launch_qgemv_bits<4>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
   }

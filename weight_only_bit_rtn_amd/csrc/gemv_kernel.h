@@ -19,7 +19,7 @@
 //    the issue arbiter favours simply takes more items and all waves finish
 //    together instead of the youngest ones running alone at the end;
 //  - lane l owns units l, l+64, ... of each row, so one load instruction of
-//    the wave reads 1 KiB (2/4-bit) or 768 B (3-bit) of contiguous packed
+//    the wave reads 1 KiB (2/4/8-bit) or 768 B (3-bit) of contiguous packed
 //    words; loads are buffer loads with the streaming (slc) cache policy,
 //    which measurably raises the HBM read rate on MI355X for data read once,
 //    through a per-row resource descriptor whose size is the row's byte
@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
           // Positions past the end of the row (last K step of a ragged row)
           // are decoded from zero words without masking: their activations
           // are staged as zeros, so only a finite decode is needed there,
-          // which |q - z| * s <= 15 * s < 65504 guarantees.
+          // which |q - z| * s <= 15 * s < 65504 guarantees (8-bit codes:
+          // the fast-path bounds z <= 255, s < 256).
           rowfast &= rows_s[r] < 0x6C00u;  // s < 4096
 #pragma unroll
           for (int i = 0; i < U::NPOS; ++i) {

@@ -16,7 +16,8 @@
 // 16 bits (2-bit) or 24 bits (3-bit; four neighbouring lanes then assemble
 // the three 32-bit words of their 32 codes with a DPP lane exchange).  The
 // whole row stays in registers between the min/max pass and the code pass, so
-// every weight is read from memory once.
+// every weight is read from memory once.  At 8 bits a chunk's codes are its 8
+// bytes in the packed row as well as in the byte-code output.
 //
 // Arithmetic.  The codes need fl32(w / s) exactly (one IEEE division per
 // weight).  With r_hi = fl32(1/s) and r_lo = fl32(fma(-s, r_hi, 1) * r_hi),
@@ -26,8 +27,8 @@
 // significands is never within 2^-36 (relative) of an fp32 rounding midpoint,
 // while the right-hand side is within 2^-45 of w / s before its single
 // rounding.  The identity was checked exhaustively over all fp16 w and all
-// positive finite fp16 s, and for d / M (fp32 d, M = 3, 7, 15) over every fp32
-// significand.  Rounding to an integer uses v + 1.5 * 2^23, whose fp32 sum
+// positive finite fp16 s, and for d / M (fp32 d, M = 3, 7, 15, 127, 255) over
+// every fp32 significand.  Rounding to an integer uses v + 1.5 * 2^23, whose fp32 sum
 // rounds v half-to-even onto the integer grid; the codes' quotients are
 // bounded by 2^16 in magnitude (the largest |w| / s of any group of finite
 // fp16 values), far inside the 2^22 range where that is exact.
@@ -129,7 +130,7 @@ struct Params {
 
 // The fp32 quotient x / D for a small constant divisor D, correctly rounded
 // (the two-term reciprocal form, checked for every fp32 significand and
-// D = 3, 7, 15; D = 1 is exact).
+// D = 3, 7, 15, 127, 255; D = 1 is exact).
 template <int D>
 __device__ __forceinline__ float div_const(float x) {
   constexpr float m_hi = 1.0f / (float)D;
@@ -180,7 +181,8 @@ __device__ __forceinline__ uint32_t code_of(_Float16 wh, const Params& p) {
   return (uint32_t)min(max((int)t, p.qlo), M);
 }
 
-// The 8 codes of a chunk, packed least significant first.
+// The 8 codes of a chunk, packed least significant first (8-bit codes do not
+// fit one word: their packed form is code_bytes).
 template <int BITS>
 __device__ __forceinline__ uint32_t chunk_codes(const u4_t& d, const Params& p, uint32_t (&q)[8]) {
 #pragma unroll
@@ -189,9 +191,12 @@ __device__ __forceinline__ uint32_t chunk_codes(const u4_t& d, const Params& p, 
     q[2 * i] = code_of<BITS>(v.x, p);
     q[2 * i + 1] = code_of<BITS>(v.y, p);
   }
-  uint32_t acc = q[0];
+  uint32_t acc = 0;
+  if constexpr (BITS < 8) {
+    acc = q[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) acc |= q[i] << (BITS * i);
+    for (int i = 1; i < 8; ++i) acc |= q[i] << (BITS * i);
+  }
   return acc;
 }
 
@@ -211,7 +216,10 @@ template <int BITS>
 struct StoreMap {
   uint32_t off, step, shift;
   __device__ __forceinline__ StoreMap(uint32_t t, uint32_t T) {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 8) {
+      off = t * 8u;
+      step = T * 8u;
+    } else if constexpr (BITS == 4) {
       off = t * 4u;
       step = T * 4u;
     } else if constexpr (BITS == 2) {
@@ -280,7 +288,11 @@ __global__ __launch_bounds__(1024) void rtn_quantize_kernel(
     if constexpr (CODES)
       __builtin_amdgcn_raw_buffer_store_b64(code_bytes(q), crs, (int)((uint32_t)(i * T + t) * 8u),
                                             0, 0);
-    store_chunk<BITS>(prs, bits, smap, (uint32_t)i);
+    if constexpr (BITS == 8)
+      __builtin_amdgcn_raw_buffer_store_b64(code_bytes(q), prs,
+                                            (int)(smap.off + (uint32_t)i * smap.step), 0, 0);
+    else
+      store_chunk<BITS>(prs, bits, smap, (uint32_t)i);
   };
 
   if constexpr (MODE == kRowGroup) {
@@ -380,6 +392,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
   // nchunks is a multiple of 4, so quads of lanes are active or idle together
   for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks; c += stride) {
     const u2_t b = *reinterpret_cast<const u2_t*>(codes + 8 * c);
+    if constexpr (BITS == 8) {  // code k is byte k of the row: a copy
+      reinterpret_cast<u2_t*>(packed)[c] = b;
+      continue;
+    }
     uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) bits |= ((b[i >> 2] >> (8 * (i & 3))) & mask) << (BITS * i);
@@ -473,6 +489,9 @@ hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, in
     case 3:
       return launch_bits<3>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
                             stream);
+    case 8:
+      return launch_bits<8>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
+                            stream);
     default:
       return launch_bits<4>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
                             stream);
@@ -491,6 +510,9 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uin
       break;
     case 3:
       hipLaunchKernelGGL(pack_kernel<3>, grid, block, 0, stream, codes, nchunks, packed);
+      break;
+    case 8:
+      hipLaunchKernelGGL(pack_kernel<8>, grid, block, 0, stream, codes, nchunks, packed);
       break;
     default:
       hipLaunchKernelGGL(pack_kernel<4>, grid, block, 0, stream, codes, nchunks, packed);

@@ -10,6 +10,7 @@
 //   2-bit: two consecutive periods, 64 codes, 4 words (one 16-byte load)
 //   3-bit: two periods a and b taken from different places of the row,
 //          3 words each (two 12-byte loads)
+//   8-bit: 16 codes, 4 words (one 16-byte load)
 //
 // A unit yields 16 or 32 "slots": pairs of codes (lo, hi) that end up in the
 // low and high fp16 halves of one 32-bit register, so that the fp16 math runs
@@ -28,6 +29,11 @@
 //
 // The activations are stored on chip in the same slot order, so no
 // per-weight shuffle is needed in the inner loop.
+//
+// 8-bit codes cannot use a shifted field (1024 + q*2^p stays below 2048 only
+// for p = 0), so each slot pairs two neighbouring bytes of one word and a
+// single byte permute drops them under the two 0x64 exponent bytes of the
+// magic register: p = 0 for every slot.
 #pragma once
 
 #include "common.h"
@@ -139,8 +145,33 @@ struct Unit<3> {
   }
 };
 
+template <>
+struct Unit<8> {
+  static constexpr int CODES = 16, WORDS = 4, SLOTS = 8, QUADS = 2, PMAX = 0;
+  static constexpr int NCONST = 1;
+  // slot s: codes 2s (low half) and 2s + 1 (high half), bytes 0, 1 (s even)
+  // or 2, 3 (s odd) of word s / 2; a quad is eight consecutive codes
+  __host__ __device__ static constexpr int lo(int s) { return 2 * s; }
+  __host__ __device__ static constexpr int hi(int s) { return 2 * s + 1; }
+  __host__ __device__ static constexpr int pos(int) { return 0; }
+  __host__ __device__ static constexpr int cset(int) { return 0; }
+  __host__ __device__ static constexpr bool uses(int p) { return p == 0; }
+  static constexpr int NPOS = 1;
+  __host__ __device__ static constexpr int pidx(int) { return 0; }
+  // v_perm_b32 selectors 0..3 pick bytes of the word, 4..7 bytes of the magic
+  // register 0x64006400 (5 and 7 are its 0x64 bytes)
+  __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
+                                                    uint32_t mg) {
+    return __builtin_amdgcn_perm(mg, w[s >> 1], (s & 1) ? 0x07030502u : 0x07010500u);
+  }
+  __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[WORDS], int c) {
+    return (w[c >> 2] >> (8 * (c & 3))) & 255u;
+  }
+};
+
 // Slot order must put the four slots of a quad on consecutive codes, both for
-// the low and the high halves: the activation staging relies on it.
+// the low and the high halves: the activation staging relies on it (8-bit
+// quads are eight consecutive codes in natural order, staged as they are).
 template <int BITS>
 constexpr bool quads_are_runs() {
   using U = Unit<BITS>;
@@ -180,9 +211,14 @@ struct Consts {
 //  scaled mode: exponent field of s >= PMAX + 1;
 //  per-position mode: s normal and s < 8, so that (q - z) * s * 2^p stays in
 //  fp16's normal range, where scaling by 2^p commutes with the rounding.
+// 8-bit codes (no shifted positions): 0 <= z <= 255 and s < 256, so that
+//  |q - z| * s < 65504 for every code (also for decoded words past the end of
+//  a row), subnormal scales included (the single fp16 multiply rounds them
+//  correctly).
 template <int BITS, bool POS>
 __device__ __forceinline__ bool half_fast(uint32_t sb, int32_t z) {
   constexpr int PMAX = Unit<BITS>::PMAX;
+  if constexpr (BITS == 8) return (uint32_t)z <= 255u && sb < 0x5C00u;
   const bool zok = (uint32_t)z <= (1023u >> PMAX);
   const bool sok = POS ? (sb >= 0x0400u && sb < 0x4800u) : (sb >= (uint32_t)(PMAX + 1) << 10);
   return zok && sok;
@@ -348,6 +384,10 @@ template <int BITS>
 __device__ __forceinline__ uint4 x_entry(const uint16_t* __restrict__ xrow, const UnitRef& u,
                                          int q, bool bvalid) {
   using U = Unit<BITS>;
+  if constexpr (BITS == 8) {  // eight consecutive activations, as stored
+    return (bvalid && u.va) ? *reinterpret_cast<const uint4*>(xrow + u.ka + 8 * q)
+                            : make_uint4(0u, 0u, 0u, 0u);
+  }
   const int c_lo = U::lo(4 * q), c_hi = U::hi(4 * q);
   const bool vl = bvalid && (BITS == 3 ? (c_lo < 32 ? u.va : u.vb) : u.va);
   const bool vh = bvalid && (BITS == 3 ? (c_hi < 32 ? u.va : u.vb) : u.va);
