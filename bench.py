@@ -120,15 +120,22 @@ def time_launches(torch, fn, count: int, spread: bool = False):
     return avg, med, ms[(len(ms) - 1) // 10], ms[(9 * (len(ms) - 1)) // 10]
 
 
+# The same shapes at 8 bits (the wider weight-only width): OPT-175B fc1 per
+# row at batch 1 and 4, the Llama-70B MLP layer in groups of 128 at 16..64.
+WIDE_LAYERS = (("opt175b_fc1_49152x12288_8bit", 49152, 12288, 8, 0, (1, 4)),
+               ("llama70b_up_28672x8192_8bit", 28672, 8192, 8, 128, (16, 32, 64)))
+
+
 def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     import synth
     stages = {}
+    wide = [synth.Layer(*spec) for spec in WIDE_LAYERS]
     # quantize + pack (reads 2 B per weight): the OPT-175B 3-bit per-row
     # layers and the Llama-70B 4-bit layer (groups of 128), on the min-max
     # grid and, for the larger two, on the signed symmetric grid
     runs = [(synth.WORKLOADS["opt175b_3bit"][0], False), (synth.WORKLOADS["opt175b_3bit"][1], False),
             (synth.WORKLOADS["opt175b_3bit"][1], True), (synth.WORKLOADS["llama70b_mlp_4bit"][0], False),
-            (synth.WORKLOADS["llama70b_mlp_4bit"][0], True)]
+            (synth.WORKLOADS["llama70b_mlp_4bit"][0], True), (wide[0], False), (wide[1], True)]
     for layer, sym in runs:
         dev = torch.device("cuda:0")
         w = torch.from_numpy(layer.weights()).to(dev)
@@ -155,7 +162,7 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
         del w, packed, scales, zeros
         torch.cuda.empty_cache()
     # every workload's products
-    for name, layers in synth.WORKLOADS.items():
+    for name, layers in list(synth.WORKLOADS.items()) + [("8bit", wide)]:
         for layer in layers:
             prep = None
             for B in layer.batches:

@@ -17,9 +17,10 @@
 //    RG groups in the round, KP = 8 / RG waves split K between them, so few
 //    groups per CU still keep all waves busy;
 //  - K is walked in tiles; a tile holds, for every K part, four lane groups
-//    times NU consecutive units (see unit_decode.h) per row;  lane l decodes
-//    row (l % 16) of its group, lane group h = l / 16 takes its NU units, so
-//    the four lanes of a row read 4 * NU * 16 contiguous bytes;
+//    times NW units (see unit_decode.h) per row;  lane l decodes row (l % 16)
+//    of its group, lane group h = l / 16 takes NW of the part's units: NW
+//    consecutive ones (2-, 3-, 4-bit), or runs of two interleaved with the
+//    other lane groups' runs (8-bit, one 128-byte line per row and load);
 //  - x for the tile (all batch rows, zero past K and past B) is staged in
 //    LDS, double buffered, already in the decode's slot order, so one MFMA A
 //    operand is one 16-byte LDS read; the next tile's weights and x are
@@ -51,8 +52,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Group layout of the scales and zeros: one per row, power-of-two groups
 // (group index by a shift), any other group size (a division), or
-// power-of-two groups at least as long as one lane's units of a step (2- and
-// 4-bit): then those units share one group, loaded once per step.
+// power-of-two groups at least as long as a lane's run of units (2-, 4- and
+// 8-bit): then the run shares one group, loaded once per run.
 enum GroupMode { kPerRow = 0, kPow2Groups = 1, kAnyGroups = 2, kWideGroups = 3 };
 
 // Scales and zeros of constant set c of unit u: its low and high halves'
@@ -98,6 +99,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   constexpr int E = 2 * BT;                 // activation entries per thread and step
   constexpr int XBUF = kTileK * BP * 2 / 16;  // 16-byte entries of one activation buffer
   static_assert(XBUF == E * kThreads, "one step's activations are E entries per thread");
+  // lanes take runs of two units (else one run of all their units per step)
+  constexpr bool kRuns2 = BITS == 8;
+  // index of the first unit of u's run (its group constants live there)
+  auto run_start = [](int u) { return kRuns2 ? (u & ~1) : 0; };
   // LDS: two activation tiles (later the partial sums), then per-wave scratch
   // of the exact decode path
   extern __shared__ uint4 lds[];
@@ -176,14 +181,22 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
       u.vb = u.kb < K;
       return u;
     };
-    // the four lanes of a row (lane groups h) read 4 * NW consecutive units
-    auto my_unit = [&](int t, int u) { return unit_at(t, (kp * 4 + h) * NW + u); };
+    // Units of a K part (4 * NW of them) go to the four lanes of a row in
+    // runs of RN: lane group h takes units 4 * RN * (u / RN) + RN * h +
+    // u % RN, and a lane's run shares its group constants.  2-, 3- and 4-bit
+    // lanes take one run of NW consecutive units (one group per step for
+    // wide groups); 8-bit lanes, with twice the bytes per code, take runs of
+    // two, so that one load instruction of the wave reads each row's eight
+    // consecutive units, one 128-byte line per row, instead of four lines.
+    const int RN = kRuns2 ? (NW >= 2 ? 2 : 1) : NW;
+    auto part_unit = [&](int u) { return 4 * RN * (u / RN) + RN * h + u % RN; };
+    auto my_unit = [&](int t, int u) { return unit_at(t, kp * 4 * NW + part_unit(u)); };
 
     struct WBuf {
       uint32_t w[NWMAX][W];
-      // grouped layouts: the units' scales and zeros (one set per step when
-      // the lane's units share a group)
-      HalfParams hp[PERROW || GM == kWideGroups ? 1 : NWMAX][NC];
+      // grouped layouts: the units' scales and zeros (wide groups: one set
+      // per run, kept at the run's first index)
+      HalfParams hp[PERROW ? 1 : NWMAX][NC];
     };
     // Weight loads of step t: always NWMAX units per lane (clamped to the row,
     // unused ones discarded), so every step issues the same number of loads.
@@ -216,10 +229,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
           for (int c = 0; c < NC; ++c)
             b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
         } else if constexpr (GM == kWideGroups) {
-          if (u == 0) {
+          if (run_start(u) == u) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-              b.hp[0][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
+              b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
           }
         }
       }
@@ -246,7 +259,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
       const int e = tid + i * kThreads;
       const int ml = e & 63, b = e >> 6;
       const int ul = ml / Q, q = ml % Q;      // unit of the step, quad
-      const int eh = (ul / NW) & 3, ekp = ul / (4 * NW), eu = ul % NW;
+      // inverse of part_unit: K part, lane group and unit index of unit ul
+      const int ekp = ul / (4 * NW), pr = ul % (4 * NW);
+      const int run = pr / (4 * RN), pw = pr % (4 * RN);
+      const int eh = pw / RN, eu = run * RN + pw % RN;
       const UnitRef ur = unit_at(0, ul);
       const int kl = unit_k<BITS>(ur, U::lo(4 * q)), kh = unit_k<BITS>(ur, U::hi(4 * q));
       xk[i][0] = b < B ? kl : K;
@@ -288,27 +304,30 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     auto compute = [&](int t, int buf, WBuf& b) {
       if (!active) return;
       const uint4* xs = lds + buf * XBUF;
-      // one group for all of the lane's units of the step: its constants are
-      // made once per step, with every position valid.  Positions past the
-      // row end (last step of a ragged row) then decode the clamped words
-      // against zero activations: only a finite decode is needed there, which
-      // the fast path's zero-point range and s < 4096 guarantee
-      // (|q - z| * s <= 15 * s < 65504).  The exact path keeps the per-unit
-      // validity.
+      // Wide groups: one group for a run of units; its constants are made
+      // once per run, with every position valid.  Positions past the row end
+      // (last step of a ragged row) then decode the clamped words against
+      // zero activations: only a finite decode is needed there, which the
+      // fast path's zero-point range and s < 4096 guarantee (|q - z| * s <=
+      // 15 * s < 65504; 8-bit: z <= 255, s < 256).  The exact path keeps the
+      // per-unit validity.
       Consts<BITS> wcc[NC];
       bool wfast = true;
-      if constexpr (GM == kWideGroups) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          HalfParams h0 = b.hp[0][c];
-          h0.v_lo = true;
-          h0.v_hi = true;
-          wfast &= make_consts<BITS, false>(h0, wcc[c]);
-          wfast &= h0.s_lo < 0x6C00u && h0.s_hi < 0x6C00u;
-        }
-      }
 #pragma unroll
       for (int u = 0; u < NWMAX; ++u) {
+        if constexpr (GM == kWideGroups) {
+          if (run_start(u) == u && u < NW) {
+            wfast = true;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              HalfParams h0 = b.hp[u][c];
+              h0.v_lo = true;
+              h0.v_hi = true;
+              wfast &= make_consts<BITS, false>(h0, wcc[c]);
+              wfast &= h0.s_lo < 0x6C00u && h0.s_hi < 0x6C00u;
+            }
+          }
+        }
         if (u < NW) {
           const UnitRef ur = my_unit(t, u);
           HalfParams hp[NC];
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
           } else if constexpr (GM == kWideGroups) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-              hp[c] = b.hp[0][c];  // the shared group; this unit's validity
+              hp[c] = b.hp[run_start(u)][c];  // the run's group; this unit's validity
               hp[c].v_lo = ur.va;
               hp[c].v_hi = ur.vb;
               cc[c] = wcc[c];
@@ -500,10 +519,10 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
-  // wide groups: a lane's units of one step (at most 4 x 32 codes at 4 bits,
-  // 2 x 64 at 2 bits, 8 x 16 at 8 bits, starting on a multiple of that span)
-  // lie in one group
-  const bool wide = bits != 3 && gshift >= 0 && gsz >= 128;
+  // wide groups: a lane's run of units (at most 4 x 32 codes at 4 bits and
+  // 2 x 64 at 2 bits per step, 2 x 16 at 8 bits, starting on a multiple of
+  // that span) lies in one group
+  const bool wide = bits != 3 && gshift >= 0 && gsz >= (bits == 8 ? 32 : 128);
   const int gm = G == 1 ? kPerRow : wide ? kWideGroups : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
 #define LOWBIT_QGEMM_GM(bits_)                                                                  \
