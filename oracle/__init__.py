@@ -59,6 +59,10 @@ class Oracle:
         lib.orc_unpack.argtypes = [vp, i64, i64, i32, vp]
         lib.orc_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i64, vp]
         lib.orc_matmul_f64.argtypes = [vp, vp, i64, i64, i64, vp]
+        lib.orc_pack_meta.argtypes = [vp, vp, i64, vp]
+        lib.orc_pack_meta.restype = ctypes.c_int64
+        lib.orc_unpack_meta.argtypes = [vp, i64, vp, vp]
+        lib.orc_unpack_meta.restype = ctypes.c_int
         for name in ("orc_quantize_rtn", "orc_quantize_rtn_sym", "orc_pack", "orc_unpack",
                      "orc_dequant", "orc_matmul_f64"):
             getattr(lib, name).restype = ctypes.c_int
@@ -115,6 +119,26 @@ class Oracle:
         _ok(self.lib.orc_unpack(packed.ctypes.data, N, K, bits, out.ctypes.data), "unpack")
         return out
 
+    def pack_meta(self, scales: np.ndarray, zeros: np.ndarray):
+        """Compact words (fp16 scale | int16 zero << 16), same shape as
+        ``scales``, and the number of zero points saturated to int16."""
+        sb = _bits16(scales)
+        zz = np.ascontiguousarray(zeros, dtype=np.int32)
+        assert sb.shape == zz.shape
+        out = np.empty(sb.shape, np.uint32)
+        n = self.lib.orc_pack_meta(sb.ctypes.data, zz.ctypes.data, sb.size, out.ctypes.data)
+        if n < 0:
+            raise ValueError("oracle pack_meta: bad argument")
+        return out, int(n)
+
+    def unpack_meta(self, meta: np.ndarray):
+        m = np.ascontiguousarray(meta, dtype=np.uint32)
+        sb = np.empty(m.shape, np.uint16)
+        zz = np.empty(m.shape, np.int32)
+        _ok(self.lib.orc_unpack_meta(m.ctypes.data, m.size, sb.ctypes.data, zz.ctypes.data),
+            "unpack_meta")
+        return sb.view(np.float16), zz
+
     def dequant(self, codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray, bits: int,
                 group_size: int) -> np.ndarray:
         codes = _c(codes, np.uint8)
@@ -159,6 +183,14 @@ def default() -> Oracle:
             _build.build()
         _DEFAULT = Oracle(path)
     return _DEFAULT
+
+
+def pack_meta(scales, zeros):
+    return default().pack_meta(scales, zeros)
+
+
+def unpack_meta(meta):
+    return default().unpack_meta(meta)
 
 
 def f16_to_f64(h):

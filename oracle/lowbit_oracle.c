@@ -256,6 +256,40 @@ int orc_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* 
 }
 
 /* ---------------------------------------------------------------------- */
+/* Compact group metadata (reading R16): one 32-bit word per group, the     */
+/* fp16 scale in bits 0-15 and the zero point as a two's-complement 16-bit  */
+/* integer in bits 16-31, in place of a 2-byte scale plus a 4-byte zero.    */
+/* Per-group parameters are what the block formats store next to the codes */
+/* (GGUF file format, quantization-type table: a block scale, and for the   */
+/* "_1" types a block minimum); this word keeps the integer zero point of    */
+/* the min-max grid instead of a float minimum, so the dequantized weights  */
+/* do not change.  A zero point outside [-32768, 32767] cannot be stored:   */
+/* it is saturated and counted.                                              */
+/* ---------------------------------------------------------------------- */
+int64_t orc_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t count,
+                      uint32_t* meta) {
+    if (!scales || !zeros || !meta || count < 0) return -1;
+    int64_t saturated = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        int32_t z = zeros[i];
+        if (z > 32767) { z = 32767; ++saturated; }
+        if (z < -32768) { z = -32768; ++saturated; }
+        uint32_t zfield = (uint32_t)(uint16_t)(int16_t)z;
+        meta[i] = (uint32_t)scales[i] | (zfield << 16);
+    }
+    return saturated;
+}
+
+int orc_unpack_meta(const uint32_t* meta, int64_t count, uint16_t* scales, int32_t* zeros) {
+    if (!meta || !scales || !zeros || count < 0) return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        scales[i] = (uint16_t)(meta[i] & 0xffffu);
+        zeros[i] = (int32_t)(int16_t)(uint16_t)(meta[i] >> 16);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Dequantization (reading R6): deq = fp16_rne((q - zero) * scale).        */
 /* ---------------------------------------------------------------------- */
 int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,

@@ -39,6 +39,11 @@ int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zer
                 int64_t N, int64_t K, int bits, int64_t group_size, uint16_t* deq);
 int orc_matmul_f64(const uint16_t* x, const uint16_t* deq, int64_t B, int64_t N, int64_t K,
                    double* y);
+/* Compact metadata words (fp16 scale | int16 zero << 16); orc_pack_meta
+ * returns the number of zero points saturated to the int16 range (or -1). */
+int64_t orc_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t count,
+                      uint32_t* meta);
+int orc_unpack_meta(const uint32_t* meta, int64_t count, uint16_t* scales, int32_t* zeros);
 
 #ifdef __cplusplus
 }

@@ -383,6 +383,49 @@ def check_sym_bruteforce(o) -> None:
 
 
 # ---------------------------------------------------------------------------
+# Compact metadata words (fp16 scale | int16 zero << 16)
+# ---------------------------------------------------------------------------
+def check_meta_words(o) -> None:
+    cases = _load("meta_words.json")["cases"]
+    for case in cases:
+        s = np.array([int(case["scale_f16_bits"], 16)], np.uint16).view(np.float16)
+        z = np.array([case["zero"]], np.int32)
+        meta, sat = o.pack_meta(s, z)
+        assert int(meta[0]) == int(case["word"], 16), case["name"]
+        assert sat == case["saturated"], case["name"]
+        s2, z2 = o.unpack_meta(meta)
+        assert s2.view(np.uint16)[0] == s.view(np.uint16)[0], case["name"]
+        assert z2[0] == max(-32768, min(32767, case["zero"])), case["name"]
+    # all cases in one call: the count adds up
+    s = np.array([int(c["scale_f16_bits"], 16) for c in cases], np.uint16).view(np.float16)
+    z = np.array([c["zero"] for c in cases], np.int32)
+    _, sat = o.pack_meta(s, z)
+    assert sat == sum(c["saturated"] for c in cases)
+
+
+def check_meta_round_trip(o) -> None:
+    """In-range zero points survive the word; out-of-range ones saturate and
+    are counted; the low half is the scale's bit pattern unchanged.  The RTN
+    zero points of 2/3/4-bit groups with hi > lo fit (|z| <= M * 2^11 <= 30720)."""
+    rng = np.random.default_rng(16)
+    sb = rng.integers(0, 0x7C00, 4000).astype(np.uint16)
+    z = rng.integers(-70000, 70000, 4000).astype(np.int32)
+    meta, sat = o.pack_meta(sb.view(np.float16), z)
+    assert np.array_equal((meta & 0xFFFF).astype(np.uint16), sb)
+    hi = (meta >> 16).astype(np.uint16).view(np.int16).astype(np.int32)
+    assert np.array_equal(hi, np.clip(z, -32768, 32767))
+    assert sat == int(np.sum((z < -32768) | (z > 32767)))
+    for label, w in _random_weight_sets(rng):
+        for bits in (2, 3, 4):
+            _, scales, zeros = o.quantize_rtn(w, bits, 32)
+            meta, sat = o.pack_meta(scales, zeros)
+            assert sat == 0, (label, bits)
+            s2, z2 = o.unpack_meta(meta)
+            assert np.array_equal(s2.view(np.uint16), scales.view(np.uint16))
+            assert np.array_equal(z2, zeros)
+
+
+# ---------------------------------------------------------------------------
 # The reference product against exact integer arithmetic
 # ---------------------------------------------------------------------------
 def check_matmul_exact(o) -> None:
@@ -414,4 +457,4 @@ ALL_CHECKS = [check_sym_worked_examples, check_sym_invariants, check_sym_scale_i
               check_sym_bruteforce, check_f16_decode, check_f16_encode, check_worked_examples,
               check_pack_closed_forms, check_pack_bigint, check_invariants,
               check_scale_is_nearest, check_dequant_is_nearest, check_rtn_bruteforce,
-              check_matmul_exact]
+              check_matmul_exact, check_meta_words, check_meta_round_trip]

@@ -45,6 +45,11 @@ MUTANTS = {
     "sym_zero_off_by_one": ("const int32_t z = 1 << (bits - 1);",
                             "const int32_t z = (1 << (bits - 1)) - 1;"),
     "sym_round_half_away": ("float r = nearbyintf(v / sc);", "float r = roundf(v / sc);"),
+    "meta_zero_not_sign_extended": ("zeros[i] = (int32_t)(int16_t)(uint16_t)(meta[i] >> 16);",
+                                    "zeros[i] = (int32_t)(meta[i] >> 16);"),
+    "meta_no_saturation": ("if (z > 32767) { z = 32767; ++saturated; }", ""),
+    "meta_fields_swapped": ("meta[i] = (uint32_t)scales[i] | (zfield << 16);",
+                            "meta[i] = zfield | ((uint32_t)scales[i] << 16);"),
 }
 
 
