@@ -145,6 +145,40 @@ LOWBIT_API int lowbit_qgemm(const void* x_f16, int64_t B, const uint32_t* packed
                  const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
                  void* y_f16, void* hip_stream);
 
+/*
+ * Compact group metadata: one 32-bit word per group, the fp16 scale's bit
+ * pattern in bits 0-15 and the zero point as a two's-complement 16-bit
+ * integer in bits 16-31 (4 bytes per group instead of 6).  Block formats keep
+ * such per-block parameters beside the codes (GGUF file format, quantization
+ * type table: block scale, and block minimum for the "_1" types); this word
+ * keeps the integer zero point, so the dequantized weights do not change.
+ *
+ * lowbit_pack_meta writes meta[N][G] from scales_f16[N][G] and zeros[N][G]
+ * (device pointers, 16-byte aligned).  A zero point outside [-32768, 32767]
+ * is saturated to the nearest end; the number of saturated groups is ADDED
+ * to *saturated_or_null (a 4-byte aligned device int32 the caller
+ * initialises; NULL: not counted).  For 2-, 3- and 4-bit groups with
+ * max > min every zero point fits (|zero| <= M * 2^11 <= 30720); constant
+ * groups of magnitude >= 32768 and far one-signed 8-bit groups may not.
+ * N == 0 or G == 0 launches nothing.
+ */
+LOWBIT_API int lowbit_pack_meta(const uint16_t* scales_f16, const int32_t* zeros, int64_t N,
+                                int64_t G, uint32_t* meta, int32_t* saturated_or_null,
+                                void* hip_stream);
+
+/*
+ * lowbit_qgemv and lowbit_qgemm with the group parameters as compact words
+ * meta[N][G] (from lowbit_pack_meta) instead of scales and zeros.  Same
+ * arguments otherwise, same contract, same results whenever no zero point was
+ * saturated.
+ */
+LOWBIT_API int lowbit_qgemv_meta(const void* x_f16, int64_t B, const uint32_t* packed,
+                                 const uint32_t* meta, int64_t N, int64_t K, int bits,
+                                 int64_t group_size, void* y_f16, void* hip_stream);
+LOWBIT_API int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* packed,
+                                 const uint32_t* meta, int64_t N, int64_t K, int bits,
+                                 int64_t group_size, void* y_f16, void* hip_stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 LOWBIT_API const char* lowbit_status_string(int status);
 

@@ -30,8 +30,9 @@ def declared_entry_points():
 
 def test_header_declares_the_abi():
     assert declared_entry_points() == sorted(
-        ["lowbit_pack", "lowbit_qgemm", "lowbit_qgemv", "lowbit_quantize_rtn",
-         "lowbit_quantize_rtn_sym", "lowbit_status_string"])
+        ["lowbit_pack", "lowbit_pack_meta", "lowbit_qgemm", "lowbit_qgemm_meta", "lowbit_qgemv",
+         "lowbit_qgemv_meta", "lowbit_quantize_rtn", "lowbit_quantize_rtn_sym",
+         "lowbit_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lw):
@@ -104,6 +105,18 @@ MIS = P + 4
     (lambda lw: lw.qgemv_raw(P, 1, None, P, P, 4, 128, 4, 0, P, None), "ARG"),
     (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 4, 0, MIS, None), "ARG"),
     (lambda lw: lw.qgemm_raw(MIS, 1, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    # compact metadata entry points
+    (lambda lw: lw.pack_meta_raw(P, P, -1, 4, P, None, None), "ARG"),
+    (lambda lw: lw.pack_meta_raw(None, P, 4, 4, P, None, None), "ARG"),
+    (lambda lw: lw.pack_meta_raw(P, P, 4, 4, MIS, None, None), "ARG"),
+    (lambda lw: lw.pack_meta_raw(P, P, 4, 4, P, P + 2, None), "ARG"),
+    (lambda lw: lw.qgemv_meta_raw(P, 16, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemv_meta_raw(P, 1, P, None, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemm_meta_raw(P, 1, P, MIS, 4, 128, 4, 0, P, None), "ARG"),
+    (lambda lw: lw.qgemm_meta_raw(P, 1, P, P, 4, 128, 5, 0, P, None), "UNSUPPORTED"),
+    (lambda lw: lw.qgemv_meta_raw(P, 1, P, P, 4, 160, 4, 64, P, None), "SHAPE"),
+    (lambda lw: lw.pack_meta_raw(None, None, 0, 4, None, None, None), "OK"),
+    (lambda lw: lw.qgemm_meta_raw(None, 0, None, None, 4, 128, 4, 0, None, None), "OK"),
     # empty problems are valid and launch nothing
     (lambda lw: lw.quantize_rtn_raw(None, 0, 128, 4, 0, None, None, None, None, None), "OK"),
     (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),

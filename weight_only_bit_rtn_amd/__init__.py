@@ -12,6 +12,8 @@ Functions mirror the C entry points:
   pack(codes, bits) -> packed
   qgemv(x, packed, scales, zeros, K, bits, group_size) -> y      (1 <= B <= 15)
   qgemm(x, packed, scales, zeros, K, bits, group_size) -> y      (any B)
+  pack_meta(scales, zeros) -> (meta, saturated)                   compact group words
+  qgemv_meta / qgemm_meta(x, packed, meta, K, bits, group_size) -> y
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ QGEMV_MAX_B = 15
 QUANTIZE_MAX_K = 131072
 
 EXPORTED = ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
-            "lowbit_status_string")
+            "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta", "lowbit_status_string")
 
 _lib = None
 
@@ -56,8 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowbit_pack.argtypes = [vp, i64, i64, i32, vp, vp]
     lib.lowbit_qgemv.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
+    lib.lowbit_pack_meta.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.lowbit_qgemv_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
+    lib.lowbit_qgemm_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     for name in ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv",
-                 "lowbit_qgemm"):
+                 "lowbit_qgemm", "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_status_string.restype = ctypes.c_char_p
@@ -135,6 +140,20 @@ def qgemm_raw(x, B, packed, scales, zeros, N, K, bits, group_size, y, stream) ->
                                        stream)
 
 
+def pack_meta_raw(scales, zeros, N, G, meta, saturated, stream) -> int:
+    return load_library().lowbit_pack_meta(scales, zeros, N, G, meta, saturated, stream)
+
+
+def qgemv_meta_raw(x, B, packed, meta, N, K, bits, group_size, y, stream) -> int:
+    return load_library().lowbit_qgemv_meta(x, B, packed, meta, N, K, bits, group_size, y,
+                                            stream)
+
+
+def qgemm_meta_raw(x, B, packed, meta, N, K, bits, group_size, y, stream) -> int:
+    return load_library().lowbit_qgemm_meta(x, B, packed, meta, N, K, bits, group_size, y,
+                                            stream)
+
+
 # ---------------------------------------------------------------------------
 # tensor front end
 # ---------------------------------------------------------------------------
@@ -209,3 +228,50 @@ def qgemm(x, packed, scales, zeros, K: int, bits: int, group_size: int, out=None
     """y = x * deq(packed)^T, fp16 [B][N], any B (matrix-core kernel)."""
     return _product(qgemm_raw, "lowbit_qgemm", x, packed, scales, zeros, K, bits, group_size,
                     out)
+
+
+def pack_meta(scales, zeros, out=None, saturated=None):
+    """Compact group words (int32 view of fp16 scale | int16 zero << 16),
+    shape of ``scales``.  ``saturated``: optional device int32 tensor of one
+    element to which the number of saturated zero points is added."""
+    torch = _torch()
+    _require_gpu_tensor(scales, "scales", torch.float16)
+    _require_gpu_tensor(zeros, "zeros", torch.int32)
+    if scales.shape != zeros.shape or scales.dim() != 2:
+        raise ValueError("scales and zeros must both be [N][G]")
+    N, G = scales.shape
+    if out is None:
+        out = torch.empty((N, G), dtype=torch.int32, device=scales.device)
+    if saturated is not None:
+        _require_gpu_tensor(saturated, "saturated", torch.int32)
+    _check(pack_meta_raw(scales.data_ptr(), zeros.data_ptr(), N, G, out.data_ptr(),
+                         _ptr(saturated), _stream_handle(scales.device)), "lowbit_pack_meta")
+    return out
+
+
+def _product_meta(raw, name, x, packed, meta, K, bits, group_size, out):
+    torch = _torch()
+    _require_gpu_tensor(x, "x", torch.float16)
+    _require_gpu_tensor(packed, "packed", torch.int32)
+    _require_gpu_tensor(meta, "meta", torch.int32)
+    B = x.shape[0]
+    N = packed.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x.shape[1] != K")
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.float16, device=x.device)
+    _check(raw(x.data_ptr(), B, packed.data_ptr(), meta.data_ptr(), N, K, bits, group_size,
+               out.data_ptr(), _stream_handle(x.device)), name)
+    return out
+
+
+def qgemv_meta(x, packed, meta, K: int, bits: int, group_size: int, out=None):
+    """qgemv with compact group words."""
+    return _product_meta(qgemv_meta_raw, "lowbit_qgemv_meta", x, packed, meta, K, bits,
+                         group_size, out)
+
+
+def qgemm_meta(x, packed, meta, K: int, bits: int, group_size: int, out=None):
+    """qgemm with compact group words."""
+    return _product_meta(qgemm_meta_raw, "lowbit_qgemm_meta", x, packed, meta, K, bits,
+                         group_size, out)

@@ -64,18 +64,19 @@ int check_shape(int64_t N, int64_t K, int bits, int64_t group_size) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP; }
 
-int check_product(const void* x, int64_t B, const uint32_t* packed, const uint16_t* scales,
+// zeros == nullptr is accepted only with meta (compact words in `scales`).
+int check_product(const void* x, int64_t B, const uint32_t* packed, const void* scales,
                   const int32_t* zeros, int64_t N, int64_t K, int bits, int64_t group_size,
-                  const void* y) {
+                  const void* y, bool meta = false) {
   int rc = check_bits(bits);
   if (rc != LOWBIT_OK) return rc;
   if (B < 0) return LOWBIT_ERR_ARG;
   rc = check_shape(N, K, bits, group_size);
   if (rc != LOWBIT_OK) return rc;
   if (N == 0 || B == 0) return LOWBIT_OK;
-  if (!x || !packed || !scales || !zeros || !y) return LOWBIT_ERR_ARG;
-  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(zeros) ||
-      !aligned16(y))
+  if (!x || !packed || !scales || (!meta && !zeros) || !y) return LOWBIT_ERR_ARG;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) ||
+      (!meta && !aligned16(zeros)) || !aligned16(y))
     return LOWBIT_ERR_ARG;
   if ((int64_t)B * N > INT32_MAX || B > INT32_MAX) return LOWBIT_ERR_SHAPE;
   return LOWBIT_OK;
@@ -141,9 +142,10 @@ int lowbit_qgemv(const void* x_f16, int64_t B, const uint32_t* packed, const uin
   const uint16_t* x = static_cast<const uint16_t*>(x_f16);
   uint16_t* y = static_cast<uint16_t*>(y_f16);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = lowbit::launch_qgemv(x, B, packed, scales_f16, zeros, N, K, bits, group_size, y, s);
+  hipError_t e =
+      lowbit::launch_qgemv(x, B, packed, scales_f16, zeros, N, K, bits, group_size, false, y, s);
   if (e == hipErrorNotSupported)  // x too large for on-chip staging: matrix-core path
-    e = lowbit::launch_qgemm(x, B, packed, scales_f16, zeros, N, K, bits, group_size, y, s);
+    e = lowbit::launch_qgemm(x, B, packed, scales_f16, zeros, N, K, bits, group_size, false, y, s);
   return hip_status(e);
 }
 
@@ -153,9 +155,49 @@ int lowbit_qgemm(const void* x_f16, int64_t B, const uint32_t* packed, const uin
   int rc = check_product(x_f16, B, packed, scales_f16, zeros, N, K, bits, group_size, y_f16);
   if (rc != LOWBIT_OK || N == 0 || B == 0) return rc;
   return hip_status(lowbit::launch_qgemm(static_cast<const uint16_t*>(x_f16), B, packed,
-                                         scales_f16, zeros, N, K, bits, group_size,
+                                         scales_f16, zeros, N, K, bits, group_size, false,
                                          static_cast<uint16_t*>(y_f16),
                                          static_cast<hipStream_t>(hip_stream)));
+}
+
+int lowbit_pack_meta(const uint16_t* scales_f16, const int32_t* zeros, int64_t N, int64_t G,
+                     uint32_t* meta, int32_t* saturated_or_null, void* hip_stream) {
+  if (N < 0 || G < 0) return LOWBIT_ERR_ARG;
+  if (N == 0 || G == 0) return LOWBIT_OK;
+  if (N > INT64_MAX / G) return LOWBIT_ERR_SHAPE;
+  if (!scales_f16 || !zeros || !meta) return LOWBIT_ERR_ARG;
+  if (!aligned16(scales_f16) || !aligned16(zeros) || !aligned16(meta) ||
+      (saturated_or_null && reinterpret_cast<uintptr_t>(saturated_or_null) % 4 != 0))
+    return LOWBIT_ERR_ARG;
+  return hip_status(lowbit::launch_pack_meta(scales_f16, zeros, N * G, meta, saturated_or_null,
+                                             static_cast<hipStream_t>(hip_stream)));
+}
+
+int lowbit_qgemv_meta(const void* x_f16, int64_t B, const uint32_t* packed, const uint32_t* meta,
+                      int64_t N, int64_t K, int bits, int64_t group_size, void* y_f16,
+                      void* hip_stream) {
+  if (B > LOWBIT_QGEMV_MAX_B) return LOWBIT_ERR_ARG;
+  int rc = check_product(x_f16, B, packed, meta, nullptr, N, K, bits, group_size, y_f16, true);
+  if (rc != LOWBIT_OK || N == 0 || B == 0) return rc;
+  const uint16_t* x = static_cast<const uint16_t*>(x_f16);
+  const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
+  uint16_t* y = static_cast<uint16_t*>(y_f16);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = lowbit::launch_qgemv(x, B, packed, m, nullptr, N, K, bits, group_size, true, y, s);
+  if (e == hipErrorNotSupported)  // x too large for on-chip staging: matrix-core path
+    e = lowbit::launch_qgemm(x, B, packed, m, nullptr, N, K, bits, group_size, true, y, s);
+  return hip_status(e);
+}
+
+int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* packed, const uint32_t* meta,
+                      int64_t N, int64_t K, int bits, int64_t group_size, void* y_f16,
+                      void* hip_stream) {
+  int rc = check_product(x_f16, B, packed, meta, nullptr, N, K, bits, group_size, y_f16, true);
+  if (rc != LOWBIT_OK || N == 0 || B == 0) return rc;
+  return hip_status(lowbit::launch_qgemm(
+      static_cast<const uint16_t*>(x_f16), B, packed, reinterpret_cast<const uint16_t*>(meta),
+      nullptr, N, K, bits, group_size, true, static_cast<uint16_t*>(y_f16),
+      static_cast<hipStream_t>(hip_stream)));
 }
 
 const char* lowbit_status_string(int status) {

@@ -59,10 +59,9 @@ enum GroupMode { kPerRow = 0, kPow2Groups = 1, kAnyGroups = 2, kWideGroups = 3 }
 // Scales and zeros of constant set c of unit u: its low and high halves'
 // groups (a position past the row end takes the last group of the row, a
 // finite scale; its weight meets a zero activation).
-template <int BITS, int GM>
-__device__ __forceinline__ HalfParams params_at(const uint16_t* __restrict__ srow,
-                                                const int32_t* __restrict__ zrow, int gsz,
-                                                int gshift, const UnitRef& u, int c, int K) {
+template <int BITS, int GM, bool META>
+__device__ __forceinline__ HalfParams params_at(const RowParams<META>& rp, int gsz, int gshift,
+                                                const UnitRef& u, int c, int K) {
   int kl, kh;
   if constexpr (BITS == 3) {
     kl = u.ka;
@@ -76,16 +75,14 @@ __device__ __forceinline__ HalfParams params_at(const uint16_t* __restrict__ sro
   const uint32_t gl = GM == kAnyGroups ? cl / (uint32_t)gsz : cl >> gshift;
   const uint32_t gh = GM == kAnyGroups ? ch / (uint32_t)gsz : ch >> gshift;
   HalfParams hp;
-  hp.s_lo = srow[gl];
-  hp.s_hi = srow[gh];
-  hp.z_lo = zrow[gl];
-  hp.z_hi = zrow[gh];
+  rp.at((int)gl, hp.s_lo, hp.z_lo);
+  rp.at((int)gh, hp.s_hi, hp.z_hi);
   hp.v_lo = kl < K;
   hp.v_hi = kh < K;
   return hp;
 }
 
-template <int BITS, int BT, int GM>
+template <int BITS, int BT, int GM, bool META>
 __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     const uint16_t* __restrict__ x, int B, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
@@ -147,15 +144,18 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
         (int)min((int64_t)rows_here * row_bytes, (int64_t)0x7fffffff));
     const auto rs = make_rsrc(reinterpret_cast<const void*>(((uint64_t)rhi << 32) | rlo), rbytes);
     const uint32_t row_off = (uint32_t)i16 * row_bytes;
-    const uint16_t* srow = scales + (int64_t)n * G;
-    const int32_t* zrow = zeros + (int64_t)n * G;
+    // META: `scales` holds compact words (see RowParams), `zeros` is unused
+    const RowParams<META> rp(scales, zeros, n, G);
 
     // per-row constants (one group per row): computed once per round
     Consts<BITS> rowc;
     bool rowfast = true;
     HalfParams rowp{};
     if constexpr (PERROW) {
-      rowp = HalfParams{srow[0], srow[0], zrow[0], zrow[0], true, true};
+      uint16_t s0;
+      int32_t z0;
+      rp.at(0, s0, z0);
+      rowp = HalfParams{s0, s0, z0, z0, true, true};
       rowfast = make_consts<BITS, false>(rowp, rowc);
       // positions past the end of the row decode garbage words against zero
       // activations: only a finite decode is needed there (|q - z| * s < 65504)
@@ -227,12 +227,12 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
         if constexpr (GM == kPow2Groups || GM == kAnyGroups) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
-            b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
+            b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
         } else if constexpr (GM == kWideGroups) {
           if (run_start(u) == u) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-              b.hp[u][c] = params_at<BITS, GM>(srow, zrow, gsz, gshift, ur, c, K);
+              b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
           }
         }
       }
@@ -465,13 +465,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   }
 }
 
-template <int BITS, int BT, int GM>
+template <int BITS, int BT, int GM, bool META>
 hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
   const size_t lds = 2 * (size_t)kTileK * 16 * BT * 2 + (size_t)kWaves * Unit<BITS>::WORDS * 64 * 4;
   if (lds > device_lds_per_block()) return hipErrorNotSupported;
-  const auto kern = qgemm_kernel<BITS, BT, GM>;
+  const auto kern = qgemm_kernel<BITS, BT, GM, META>;
   // the LDS request exceeds the default limit: raise it once per device
   static int raised[64] = {0};
   int dev = 0;
@@ -490,7 +490,7 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
   return hipGetLastError();
 }
 
-template <int BITS, int GM>
+template <int BITS, int GM, bool META>
 hipError_t launch_bits(int B, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                        const int32_t* zeros, int N, int K, int G, int gsz, int gshift,
                        uint16_t* y, hipStream_t stream) {
@@ -501,21 +501,66 @@ hipError_t launch_bits(int B, const uint16_t* x, const uint32_t* packed, const u
     uint16_t* yb = y + (int64_t)b0 * N;
     hipError_t e;
     if (bc <= 16)
-      e = launch_t<BITS, 1, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+      e = launch_t<BITS, 1, GM, META>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb,
+                                      stream);
     else if (bc <= 32)
-      e = launch_t<BITS, 2, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+      e = launch_t<BITS, 2, GM, META>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb,
+                                      stream);
     else
-      e = launch_t<BITS, 4, GM>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb, stream);
+      e = launch_t<BITS, 4, GM, META>(xb, bc, packed, scales, zeros, N, K, G, gsz, gshift, yb,
+                                      stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Group layout dispatch of one width (wide groups do not apply to 3-bit).
+template <int BITS, bool META>
+hipError_t launch_layout(int gm, int B, const uint16_t* x, const uint32_t* packed,
+                         const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
+                         int gsz, int gshift, uint16_t* y, hipStream_t stream) {
+  switch (gm) {
+    case kPerRow:
+      return launch_bits<BITS, kPerRow, META>(B, x, packed, scales, zeros, N, K, G, gsz, gshift,
+                                              y, stream);
+    case kPow2Groups:
+      return launch_bits<BITS, kPow2Groups, META>(B, x, packed, scales, zeros, N, K, G, gsz,
+                                                  gshift, y, stream);
+    case kWideGroups:
+      return launch_bits<BITS, (BITS == 3 ? kPow2Groups : kWideGroups), META>(
+          B, x, packed, scales, zeros, N, K, G, gsz, gshift, y, stream);
+    default:
+      return launch_bits<BITS, kAnyGroups, META>(B, x, packed, scales, zeros, N, K, G, gsz,
+                                                 gshift, y, stream);
+  }
+}
+
+template <bool META>
+hipError_t launch_width(int bits, int gm, int B, const uint16_t* x, const uint32_t* packed,
+                        const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
+                        int gsz, int gshift, uint16_t* y, hipStream_t stream) {
+  switch (bits) {
+    case 2:
+      return launch_layout<2, META>(gm, B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
+                                    stream);
+    case 3:
+      return launch_layout<3, META>(gm, B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
+                                    stream);
+    case 8:
+      return launch_layout<8, META>(gm, B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
+                                    stream);
+    default:
+      return launch_layout<4, META>(gm, B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
+                                    stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
-                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream) {
+                        int bits, int64_t group_size, bool meta, uint16_t* y,
+                        hipStream_t stream) {
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
@@ -525,32 +570,10 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const bool wide = bits != 3 && gshift >= 0 && gsz >= (bits == 8 ? 32 : 128);
   const int gm = G == 1 ? kPerRow : wide ? kWideGroups : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
-#define LOWBIT_QGEMM_GM(bits_)                                                                  \
-  switch (gm) {                                                                                 \
-    case kPerRow:                                                                               \
-      return launch_bits<bits_, kPerRow>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y,   \
-                                         stream);                                               \
-    case kPow2Groups:                                                                           \
-      return launch_bits<bits_, kPow2Groups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift,  \
-                                             y, stream);                                        \
-    case kWideGroups:                                                                           \
-      return launch_bits<bits_, (bits_ == 3 ? kPow2Groups : kWideGroups)>(                       \
-          b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);                        \
-    default:                                                                                    \
-      return launch_bits<bits_, kAnyGroups>(b, x, packed, scales, zeros, n, k, G, gsz, gshift, y, \
-                                            stream);                                            \
-  }
-  switch (bits) {
-    case 2:
-      LOWBIT_QGEMM_GM(2)
-    case 3:
-      LOWBIT_QGEMM_GM(3)
-    case 8:
-      LOWBIT_QGEMM_GM(8)
-    default:
-      LOWBIT_QGEMM_GM(4)
-  }
-#undef LOWBIT_QGEMM_GM
+  return meta ? launch_width<true>(bits, gm, b, x, packed, scales, zeros, n, k, G, gsz, gshift, y,
+                                   stream)
+              : launch_width<false>(bits, gm, b, x, packed, scales, zeros, n, k, G, gsz, gshift,
+                                    y, stream);
 }
 
 }  // namespace lowbit

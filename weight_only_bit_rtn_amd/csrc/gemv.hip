@@ -12,13 +12,14 @@ namespace lowbit {
 template <int BITS>
 hipError_t launch_qgemv_bits(const uint16_t* x, int B, const uint32_t* packed,
                              const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
-                             int gsz, int gshift, uint16_t* y, hipStream_t stream);
+                             int gsz, int gshift, bool meta, uint16_t* y, hipStream_t stream);
 
 constexpr int kGemvMaxValuBatch = 8;
 
 hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
-                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream) {
+                        int bits, int64_t group_size, bool meta, uint16_t* y,
+                        hipStream_t stream) {
   if (B > kGemvMaxValuBatch) return hipErrorNotSupported;
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
@@ -26,13 +27,17 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int b = (int)B, n = (int)N, k = (int)K;
   switch (bits) {
     case 2:
-      return launch_qgemv_bits<2>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      return launch_qgemv_bits<2>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
+                                  stream);
     case 3:
-      return launch_qgemv_bits<3>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      return launch_qgemv_bits<3>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
+                                  stream);
     case 8:
-      return launch_qgemv_bits<8>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      return launch_qgemv_bits<8>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
+                                  stream);
     default:
-      return launch_qgemv_bits<4>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, y, stream);
+      return launch_qgemv_bits<4>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
+                                  stream);
   }
 }
 

@@ -3,6 +3,6 @@
 
 namespace lowbit {
 template hipError_t launch_qgemv_bits<2>(const uint16_t*, int, const uint32_t*, const uint16_t*,
-                                          const int32_t*, int, int, int, int, int, uint16_t*,
-                                          hipStream_t);
+                                          const int32_t*, int, int, int, int, int, bool,
+                                          uint16_t*, hipStream_t);
 }  // namespace lowbit

@@ -195,7 +195,7 @@ struct Item {
   __amdgpu_buffer_rsrc_t rs[R];
 };
 
-template <int BITS, int BB, int R, bool PERROW, bool SPLIT>
+template <int BITS, int BB, int R, bool PERROW, bool SPLIT, bool META>
 __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
@@ -254,8 +254,11 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     int32_t z[R][NL];
   };
 
-  const auto srs = rsrc(scales, (uint32_t)min((int64_t)N * G * 2, (int64_t)0x7fffffff));
-  const auto zrs = rsrc(zeros, (uint32_t)min((int64_t)N * G * 4, (int64_t)0x7fffffff));
+  // META: `scales` holds the compact words (4 bytes per group) and the
+  // zeros descriptor is empty
+  const auto srs =
+      rsrc(scales, (uint32_t)min((int64_t)N * G * (META ? 4 : 2), (int64_t)0x7fffffff));
+  const auto zrs = rsrc(zeros, META ? 0u : (uint32_t)min((int64_t)N * G * 4, (int64_t)0x7fffffff));
   int rt0 = t0;  // first tile of the current round
   int nit = 0;   // items of the current round
 
@@ -305,19 +308,23 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
           // lgkm counter with the LDS activation reads, and every wait on
           // those would then also wait for this prefetch to come from HBM
           const uint32_t nn = (uint32_t)n + 0u * (uint32_t)lane;
-          b.s[r][0] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * nn, 0, 0);
-          b.z[r][0] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(zrs, 4u * nn, 0, 0);
+          if constexpr (META) {
+            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(srs, 4u * nn, 0, 0);
+            b.s[r][0] = (uint16_t)v;
+            b.z[r][0] = (int32_t)v >> 16;
+          } else {
+            b.s[r][0] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * nn, 0, 0);
+            b.z[r][0] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(zrs, 4u * nn, 0, 0);
+          }
         }
       } else {
-        const uint16_t* srow = scales + (int64_t)n * G;
-        const int32_t* zrow = zeros + (int64_t)n * G;
+        const RowParams<META> rp(scales, zeros, n, G);
 #pragma unroll
         for (int c = 0; c < NL; ++c) {
           const int kk = BITS == 3 ? (c == 0 ? u.ka : u.kb) : u.ka + 32 * c;
           const bool v = BITS == 3 ? (c == 0 ? u.va : u.vb) : u.va;
           const int g = v ? group_of(kk, gsz, gshift) : 0;
-          b.s[r][c] = srow[g];
-          b.z[r][c] = zrow[g];
+          rp.at(g, b.s[r][c], b.z[r][c]);
         }
       }
     }
@@ -567,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   }
 }
 
-template <int BITS, int BB, bool PERROW, bool SPLIT>
+template <int BITS, int BB, bool PERROW, bool SPLIT, bool META>
 hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
@@ -592,7 +599,7 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
                      (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) +
                      (size_t)RT * R * BB * JC * sizeof(float) + 16;
   if (lds > device_lds_per_block() || lds > kLdsBudget) return hipErrorNotSupported;
-  const auto kern = qgemv_kernel<BITS, BB, R, PERROW, SPLIT>;
+  const auto kern = qgemv_kernel<BITS, BB, R, PERROW, SPLIT, META>;
   if (lds > 64 * 1024) {
     // above the default limit: raise it (once per device) to the largest
     // request this kernel can make
@@ -612,14 +619,14 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   return hipGetLastError();
 }
 
-template <int BITS, bool PERROW, bool SPLIT>
+template <int BITS, bool PERROW, bool SPLIT, bool META>
 hipError_t launch_bits(int B, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                        const int32_t* zeros, int N, int K, int G, int gsz, int gshift,
                        uint16_t* y, hipStream_t stream) {
 #define LOWBIT_GEMV_CASE(bb)                                                                  \
   case bb:                                                                                    \
-    return launch_t<BITS, bb, PERROW, SPLIT>(x, packed, scales, zeros, N, K, G, gsz, gshift, \
-                                             y, stream);
+    return launch_t<BITS, bb, PERROW, SPLIT, META>(x, packed, scales, zeros, N, K, G, gsz,  \
+                                                   gshift, y, stream);
   switch (B) {
     LOWBIT_GEMV_CASE(1)
     LOWBIT_GEMV_CASE(2)
@@ -637,22 +644,35 @@ hipError_t launch_bits(int B, const uint16_t* x, const uint32_t* packed, const u
 
 }  // namespace gemv_detail
 
-// Per-width entry (instantiated in gemv2.hip, gemv3.hip, gemv4.hip).
+// Per-width entry (instantiated in gemv2.hip, gemv3.hip, gemv4.hip,
+// gemv8.hip).  meta: `scales` holds compact words (see RowParams), `zeros`
+// is unused.
+template <int BITS, bool META>
+hipError_t launch_qgemv_layout(const uint16_t* x, int B, const uint32_t* packed,
+                               const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
+                               int gsz, int gshift, uint16_t* y, hipStream_t stream) {
+  using namespace gemv_detail;
+  if (G == 1)
+    return launch_bits<BITS, true, false, META>(B, x, packed, scales, zeros, N, K, G, gsz, gshift,
+                                                y, stream);
+  if constexpr (BITS == 2) {
+    if (gsz % 64 != 0)
+      return launch_bits<2, false, true, META>(B, x, packed, scales, zeros, N, K, G, gsz, gshift,
+                                               y, stream);
+  }
+  return launch_bits<BITS, false, false, META>(B, x, packed, scales, zeros, N, K, G, gsz, gshift,
+                                               y, stream);
+}
+
 template <int BITS>
 hipError_t launch_qgemv_bits(const uint16_t* x, int B, const uint32_t* packed,
                              const uint16_t* scales, const int32_t* zeros, int N, int K,
-                             int G, int gsz, int gshift, uint16_t* y, hipStream_t stream) {
-  using namespace gemv_detail;
-  if (G == 1)
-    return launch_bits<BITS, true, false>(B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
-                                          stream);
-  if constexpr (BITS == 2) {
-    if (gsz % 64 != 0)
-      return launch_bits<2, false, true>(B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
-                                         stream);
-  }
-  return launch_bits<BITS, false, false>(B, x, packed, scales, zeros, N, K, G, gsz, gshift, y,
-                                         stream);
+                             int G, int gsz, int gshift, bool meta, uint16_t* y,
+                             hipStream_t stream) {
+  return meta ? launch_qgemv_layout<BITS, true>(x, B, packed, scales, zeros, N, K, G, gsz, gshift,
+                                                y, stream)
+              : launch_qgemv_layout<BITS, false>(x, B, packed, scales, zeros, N, K, G, gsz,
+                                                 gshift, y, stream);
 }
 
 }  // namespace lowbit

@@ -6,8 +6,6 @@
 
 namespace lowbit {
 
-size_t quantize_lds_bytes(int64_t K, int64_t G);
-
 // Min-max grid (sym = false) or signed symmetric grid (sym = true).
 hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, int64_t group_size,
                            bool sym, uint8_t* codes, uint32_t* packed, uint16_t* scales,
@@ -16,14 +14,24 @@ hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, in
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,
                        hipStream_t stream);
 
+// Compact group words from separate scales and zeros (zero points saturated
+// to int16, counted into *saturated when it is non-null).
+hipError_t launch_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t count,
+                            uint32_t* meta, int32_t* saturated, hipStream_t stream);
+
+// The products take the group parameters as separate scales and zeros, or
+// (meta = true) as compact words passed through `scales` (zeros unused).
+
 // VALU dequant-GEMV; returns hipErrorNotSupported when x does not fit the
 // on-chip staging budget (the caller then uses the MFMA path).
 hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
-                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream);
+                        int bits, int64_t group_size, bool meta, uint16_t* y,
+                        hipStream_t stream);
 
 hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
-                        int bits, int64_t group_size, uint16_t* y, hipStream_t stream);
+                        int bits, int64_t group_size, bool meta, uint16_t* y,
+                        hipStream_t stream);
 
 }  // namespace lowbit

@@ -412,6 +412,27 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
   }
 }
 
+// Compact group words: fp16 scale bits | int16 zero point << 16, the zero
+// saturated to the int16 range; each wave adds its saturation count to
+// *saturated once.
+__global__ __launch_bounds__(256) void pack_meta_kernel(const uint16_t* __restrict__ scales,
+                                                        const int32_t* __restrict__ zeros,
+                                                        int64_t count, uint32_t* __restrict__ meta,
+                                                        int32_t* __restrict__ saturated) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int sat = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < count; i += stride) {
+    const int32_t z = zeros[i];
+    const int32_t zc = min(max(z, -32768), 32767);
+    sat += zc != z ? 1 : 0;
+    meta[i] = (uint32_t)scales[i] | ((uint32_t)(uint16_t)(int16_t)zc << 16);
+  }
+  if (saturated) {
+    for (int o = kWave / 2; o > 0; o >>= 1) sat += __shfl_xor(sat, o);
+    if ((threadIdx.x & (kWave - 1)) == 0 && sat != 0) atomicAdd(saturated, sat);
+  }
+}
+
 constexpr int kChunkCounts[] = {1, 2, 4, 6, 8, 16};
 
 template <int BITS, int MODE>
@@ -496,6 +517,16 @@ hipError_t launch_quantize(const uint16_t* w, int64_t N, int64_t K, int bits, in
       return launch_bits<4>(w, N, (int)K, G, cpg, T, nl, sym ? 1 : 0, codes, packed, scales, zeros,
                             stream);
   }
+}
+
+hipError_t launch_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t count,
+                            uint32_t* meta, int32_t* saturated, hipStream_t stream) {
+  const int64_t want = (count + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const dim3 grid((unsigned)(want < cap ? want : cap)), block(256);
+  hipLaunchKernelGGL(pack_meta_kernel, grid, block, 0, stream, scales, zeros, count, meta,
+                     saturated);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed,

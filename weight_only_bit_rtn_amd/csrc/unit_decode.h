@@ -184,6 +184,36 @@ constexpr bool quads_are_runs() {
 static_assert(quads_are_runs<2>() && quads_are_runs<3>() && quads_are_runs<4>(),
               "slot order breaks the activation staging");
 
+// Group parameters of one weight row: a scale array and a zero array, or
+// (META) one compact word per group with the fp16 scale in bits 0..15 and the
+// zero point as a 16-bit two's-complement integer in bits 16..31.  With META
+// the words arrive through the `scales` pointer and `zeros` is unused.
+template <bool META>
+struct RowParams {
+  const uint16_t* s = nullptr;
+  const int32_t* z = nullptr;
+  const uint32_t* m = nullptr;
+  __device__ __forceinline__ RowParams(const uint16_t* scales, const int32_t* zeros, int64_t n,
+                                       int G) {
+    if constexpr (META) {
+      m = reinterpret_cast<const uint32_t*>(scales) + n * G;
+    } else {
+      s = scales + n * G;
+      z = zeros + n * G;
+    }
+  }
+  __device__ __forceinline__ void at(int g, uint16_t& sb, int32_t& zz) const {
+    if constexpr (META) {
+      const uint32_t v = m[g];
+      sb = (uint16_t)v;
+      zz = (int32_t)v >> 16;
+    } else {
+      sb = s[g];
+      zz = z[g];
+    }
+  }
+};
+
 // Raw per-half quantization parameters (scale bits, zero, lane validity).
 struct HalfParams {
   uint16_t s_lo, s_hi;
