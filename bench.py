@@ -61,6 +61,12 @@ def product_bytes(N: int, K: int, bits: int, group_size: int, B: int) -> int:
     return N * K * bits // 8 + N * G * 2 + N * G * 4 + B * K * 2 + B * N * 2
 
 
+def product_bytes_meta(N: int, K: int, bits: int, group_size: int, B: int) -> int:
+    """Algorithmic bytes with compact group words (4 bytes per group)."""
+    G = 1 if group_size == 0 else K // group_size
+    return N * K * bits // 8 + N * G * 4 + B * K * 2 + B * N * 2
+
+
 def quantize_bytes(N: int, K: int, bits: int, group_size: int) -> int:
     G = 1 if group_size == 0 else K // group_size
     return N * K * 2 + N * K * bits // 8 + N * G * 6
@@ -84,6 +90,10 @@ class Prepared:
                   for B in layer.batches}
         self.np = np
 
+    def add_meta(self, lw) -> None:
+        """Compact group words for every copy (4th element of each copy)."""
+        self.copies = [(p, s, z, lw.pack_meta(s, z)) for (p, s, z) in self.copies]
+
     def footprint(self) -> int:
         L = self.layer
         return product_bytes(L.N, L.K, L.bits, L.group_size, 0)
@@ -95,7 +105,15 @@ def copies_for(footprint: int) -> int:
 
 def run_product(lw, prep: Prepared, B: int, c: int, stream: int, kernel: str) -> None:
     L = prep.layer
-    packed, scales, zeros = prep.copies[c % len(prep.copies)]
+    cp = prep.copies[c % len(prep.copies)]
+    packed, scales, zeros = cp[:3]
+    if kernel.endswith("_meta"):
+        raw = lw.qgemv_meta_raw if kernel == "qgemv_meta" else lw.qgemm_meta_raw
+        st = raw(prep.x[B].data_ptr(), B, packed.data_ptr(), cp[3].data_ptr(), L.N, L.K, L.bits,
+                 L.group_size, prep.y[B].data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"{kernel} failed: {lw.status_string(st)}")
+        return
     raw = lw.qgemv_raw if kernel == "qgemv" else lw.qgemm_raw
     st = raw(prep.x[B].data_ptr(), B, packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
              L.N, L.K, L.bits, L.group_size, prep.y[B].data_ptr(), stream)
@@ -165,22 +183,27 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     for name, layers in list(synth.WORKLOADS.items()) + [("8bit", wide)]:
         for layer in layers:
             prep = None
-            for B in layer.batches:
-                kern = "qgemv" if B <= lw.QGEMV_MAX_B else "qgemm"
+            # grouped layers are also timed with compact group words
+            variants = ("", "_meta") if layer.group_size > 0 and layer.bits != 8 else ("",)
+            for B, var in [(B, v) for v in variants for B in layer.batches]:
+                kern = ("qgemv" if B <= lw.QGEMV_MAX_B else "qgemm") + var
                 if prep is None:
                     fp = product_bytes(layer.N, layer.K, layer.bits, layer.group_size, 0)
                     prep = Prepared(lw, torch, layer, copies_for(fp))
+                    if len(variants) > 1:
+                        prep.add_meta(lw)
                 for i in range(3):
                     run_product(lw, prep, B, i, stream, kern)
                 avg, med, p10, p90 = time_launches(
                     torch, lambda i: run_product(lw, prep, B, i, stream, kern), reps, spread=True)
-                nbytes = product_bytes(layer.N, layer.K, layer.bits, layer.group_size, B)
+                nbytes = (product_bytes_meta if var else product_bytes)(
+                    layer.N, layer.K, layer.bits, layer.group_size, B)
                 gbps = nbytes / (avg * 1e-3) / 1e9
                 rec = {"kernel": kern, "us": round(avg * 1e3, 2), "us_median": round(med * 1e3, 2),
                        "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
                        "bytes": nbytes, "GBps": round(gbps, 1),
                        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-                if kern == "qgemm":
+                if kern.startswith("qgemm"):
                     tflops = 2.0 * B * layer.N * layer.K / (avg * 1e-3) / 1e12
                     rec["TFLOPs"] = round(tflops, 1)
                     rec["mfma_frac"] = round(tflops / MFMA_F16_PEAK_TFLOPS, 4)
