@@ -63,6 +63,10 @@ class Oracle:
         lib.orc_pack_meta.restype = ctypes.c_int64
         lib.orc_unpack_meta.argtypes = [vp, i64, vp, vp]
         lib.orc_unpack_meta.restype = ctypes.c_int
+        lib.orc_hessian.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+        lib.orc_hessian.restype = ctypes.c_int
+        lib.orc_quantize_gptq.argtypes = [vp, i64, i64, vp, i32, i64, vp, vp, vp, vp]
+        lib.orc_quantize_gptq.restype = ctypes.c_int
         for name in ("orc_quantize_rtn", "orc_quantize_rtn_sym", "orc_pack", "orc_unpack",
                      "orc_dequant", "orc_matmul_f64"):
             getattr(lib, name).restype = ctypes.c_int
@@ -118,6 +122,31 @@ class Oracle:
         out = np.empty((N, K), np.uint8)
         _ok(self.lib.orc_unpack(packed.ctypes.data, N, K, bits, out.ctypes.data), "unpack")
         return out
+
+    def hessian(self, x: np.ndarray, damp: float) -> np.ndarray:
+        """H = (2/n) X^T X + damp * mean(diag) * I for fp16 x[n][K], fp64."""
+        xb = _bits16(x)
+        n, K = xb.shape
+        H = np.empty((K, K), np.float64)
+        _ok(self.lib.orc_hessian(xb.ctypes.data, n, K, float(damp), H.ctypes.data), "hessian")
+        return H
+
+    def quantize_gptq(self, w: np.ndarray, H: np.ndarray, bits: int, group_size: int):
+        """Error-feedback codes of fp16 w[N][K] on the RTN grid of w, with the
+        Hessian H[K][K]; returns (codes, scales, zeros) as quantize_rtn."""
+        wb = _bits16(w)
+        N, K = wb.shape
+        Hc = np.ascontiguousarray(H, dtype=np.float64)
+        assert Hc.shape == (K, K)
+        G = groups(K, group_size)
+        codes = np.empty((N, K), np.uint8)
+        scales = np.empty((N, G), np.uint16)
+        zeros = np.empty((N, G), np.int32)
+        work = np.empty(3 * K * K + N * K, np.float64)
+        _ok(self.lib.orc_quantize_gptq(wb.ctypes.data, N, K, Hc.ctypes.data, bits, group_size,
+                                       codes.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
+                                       work.ctypes.data), "quantize_gptq")
+        return codes, scales.view(np.float16), zeros
 
     def pack_meta(self, scales: np.ndarray, zeros: np.ndarray):
         """Compact words (fp16 scale | int16 zero << 16), same shape as
@@ -191,6 +220,14 @@ def pack_meta(scales, zeros):
 
 def unpack_meta(meta):
     return default().unpack_meta(meta)
+
+
+def hessian(x, damp):
+    return default().hessian(x, damp)
+
+
+def quantize_gptq(w, H, bits, group_size):
+    return default().quantize_gptq(w, H, bits, group_size)
 
 
 def f16_to_f64(h):

@@ -290,6 +290,111 @@ int orc_unpack_meta(const uint32_t* meta, int64_t count, uint16_t* scales, int32
 }
 
 /* ---------------------------------------------------------------------- */
+/* Error-feedback quantization (GPTQ / OPTQ), readings R17-R20.            */
+/* BladeLLM model quantization, "Quantization algorithms", GPTQ: the       */
+/* parameters of a channel are quantized one after another, and the       */
+/* inverse of the Hessian built from the layer's input activations is used */
+/* to adjust the parameters not yet quantized, compensating the error.     */
+/* OPTQ reproducibility card, "Experiment Setup" row: layer Hessians are   */
+/* accumulated from calibration inputs; per-row asymmetric min-max grid.   */
+/* ---------------------------------------------------------------------- */
+
+/* H = (2/n) X^T X for calibration inputs x[n][K] (fp16), in fp64, plus      */
+/* damp * mean(diag H) on the diagonal (R17).                               */
+int orc_hessian(const uint16_t* x, int64_t n, int64_t K, double damp, double* H) {
+    if (!x || !H || n <= 0 || K <= 0 || damp < 0) return -1;
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < K; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < n; ++t)
+                acc += orc_f16_to_f64(x[t * K + i]) * orc_f16_to_f64(x[t * K + j]);
+            H[i * K + j] = 2.0 * acc / (double)n;
+        }
+    double tr = 0.0;
+    for (int64_t i = 0; i < K; ++i) tr += H[i * K + i];
+    const double add = damp * tr / (double)K;
+    for (int64_t i = 0; i < K; ++i) H[i * K + i] += add;
+    return 0;
+}
+
+/* Inverse of a symmetric positive definite matrix by Gauss-Jordan          */
+/* elimination on [A | I] (no pivoting: the pivots of an SPD matrix are      */
+/* positive).  Returns -1 on a non-positive pivot.                          */
+static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < K; ++j) {
+            work[i * K + j] = A[i * K + j];
+            inv[i * K + j] = (i == j) ? 1.0 : 0.0;
+        }
+    for (int64_t c = 0; c < K; ++c) {
+        const double p = work[c * K + c];
+        if (!(p > 0.0)) return -1;
+        for (int64_t j = 0; j < K; ++j) {
+            work[c * K + j] /= p;
+            inv[c * K + j] /= p;
+        }
+        for (int64_t r = 0; r < K; ++r) {
+            if (r == c) continue;
+            const double f = work[r * K + c];
+            if (f == 0.0) continue;
+            for (int64_t j = 0; j < K; ++j) {
+                work[r * K + j] -= f * work[c * K + j];
+                inv[r * K + j] -= f * inv[c * K + j];
+            }
+        }
+    }
+    return 0;
+}
+
+/* GPTQ codes for w[N][K] given the Hessian H[K][K] (R18-R20):               */
+/*  - the grid (scales, zeros) is the min-max RTN grid of the ORIGINAL       */
+/*    weights, per row or per group, exactly as orc_quantize_rtn;           */
+/*  - columns are taken in their natural order i = 0 .. K-1;                */
+/*  - at column i, with Hinv the inverse Hessian of the columns not yet      */
+/*    quantized: q = clamp(rint(w_i / s) + z, 0, M) on the current fp64     */
+/*    weight, deq = fp16_rne((q - z) * s), err = (w_i - deq) / Hinv[i][i],  */
+/*    w_j -= err * Hinv[i][j] for every later column j, then column i is     */
+/*    removed from Hinv: Hinv[j][k] -= Hinv[j][i] * Hinv[i][k] / Hinv[i][i]. */
+/* Rows are independent, so any subset of rows may be passed.              */
+int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                      int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
+                      double* work /* 3*K*K + N*K doubles */) {
+    if (!w || !H || !codes || !scales || !zeros || !work || N < 0 || K <= 0) return -1;
+    if (orc_quantize_rtn(w, N, K, bits, group_size, codes, scales, zeros) != 0) return -1;
+    const int64_t g = group_size == 0 ? K : group_size;
+    const int64_t G = groups_of(K, group_size);
+    const int M = (1 << bits) - 1;
+    double* hinv = work;
+    double* tmp = work + K * K;
+    double* cur = work + 3 * K * K;
+    if (spd_inverse(H, K, hinv, tmp) != 0) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) cur[n * K + k] = orc_f16_to_f64(w[n * K + k]);
+    for (int64_t i = 0; i < K; ++i) {
+        const double hii = hinv[i * K + i];
+        if (!(hii > 0.0)) return -1;
+        for (int64_t n = 0; n < N; ++n) {
+            const double s = orc_f16_to_f64(scales[n * G + i / g]);
+            const int64_t z = zeros[n * G + i / g];
+            const double v = cur[n * K + i];
+            int64_t q = (int64_t)nearbyint(v / s) + z;
+            if (q < 0) q = 0;
+            if (q > M) q = M;
+            codes[n * K + i] = (uint8_t)q;
+            const double deq = orc_f16_to_f64(orc_f64_to_f16((double)(q - z) * s));
+            const double err = (v - deq) / hii;
+            for (int64_t j = i + 1; j < K; ++j) cur[n * K + j] -= err * hinv[i * K + j];
+        }
+        for (int64_t j = i + 1; j < K; ++j) {
+            const double f = hinv[j * K + i] / hii;
+            if (f == 0.0) continue;
+            for (int64_t k = i + 1; k < K; ++k) hinv[j * K + k] -= f * hinv[i * K + k];
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
 /* Dequantization (reading R6): deq = fp16_rne((q - zero) * scale).        */
 /* ---------------------------------------------------------------------- */
 int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,

@@ -45,6 +45,16 @@ int64_t orc_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t coun
                       uint32_t* meta);
 int orc_unpack_meta(const uint32_t* meta, int64_t count, uint16_t* scales, int32_t* zeros);
 
+/* Error-feedback (GPTQ) quantization.  orc_hessian: H[K][K] = (2/n) X^T X
+ * for x[n][K] (fp16) plus damp * mean(diag) on the diagonal.
+ * orc_quantize_gptq: codes on the RTN grid of the original weights, chosen
+ * column by column with inverse-Hessian error feedback; `work` holds
+ * 3*K*K + N*K doubles. */
+int orc_hessian(const uint16_t* x, int64_t n, int64_t K, double damp, double* H);
+int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                      int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
+                      double* work);
+
 #ifdef __cplusplus
 }
 #endif

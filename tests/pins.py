@@ -426,6 +426,146 @@ def check_meta_round_trip(o) -> None:
 
 
 # ---------------------------------------------------------------------------
+# Error-feedback (GPTQ) quantization
+# ---------------------------------------------------------------------------
+def _hadamard(n: int) -> np.ndarray:
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def check_gptq_worked_example(o) -> None:
+    for case in _load("gptq_worked_example.json")["cases"]:
+        x = np.array(case["x"], np.float16)
+        w = np.array([case["w"]], np.float16)
+        H = o.hessian(x, case["damp"])
+        assert np.array_equal(H, np.array(case["hessian"])), case["name"]
+        codes, _, _ = o.quantize_gptq(w, H, case["bits"], 0)
+        assert codes[0].tolist() == case["gptq_codes"], case["name"]
+        rtn, _, _ = o.quantize_rtn(w, case["bits"], 0)
+        assert rtn[0].tolist() == case["rtn_codes"], case["name"]
+
+
+def check_gptq_hessian_closed_form(o) -> None:
+    """Hadamard calibration rows: X^T X = n I exactly, so H = 2 I + 2 damp I."""
+    for K in (16, 64):
+        x = _hadamard(K).astype(np.float16)
+        for damp in (0.0, 0.01, 0.25):
+            H = o.hessian(x, damp)
+            assert np.array_equal(H, np.eye(K) * (2.0 + 2.0 * damp)), (K, damp)
+        # scaled columns: X^T X = n diag(c^2)
+        c = np.array([1.0, 2.0, 0.5, 4.0] * (K // 4))
+        H = o.hessian((x * c).astype(np.float16), 0.0)
+        assert np.array_equal(H, np.diag(2.0 * c * c)), K
+
+
+def check_gptq_uncoupled_is_rtn(o) -> None:
+    """With a diagonal Hessian no error reaches another column: the codes are
+    the round-to-nearest codes (the fp64 and fp32 quotients give the same
+    integers for these weights), on the same grid."""
+    rng = np.random.default_rng(1717)
+    K = 64
+    had = _hadamard(K)
+    for trial in range(8):
+        c = rng.choice([0.5, 1.0, 2.0, 4.0], K)
+        H = o.hessian((had * c).astype(np.float16), (0.0, 0.01)[trial % 2])
+        w = (rng.standard_normal((6, K)) * 0.02).astype(np.float16)
+        for bits in (2, 3, 4, 8):
+            for g in (0, 16, 32):
+                codes, scales, zeros = o.quantize_gptq(w, H, bits, g)
+                rcodes, rscales, rzeros = o.quantize_rtn(w, bits, g)
+                assert np.array_equal(codes, rcodes), (trial, bits, g)
+                assert np.array_equal(scales.view(np.uint16), rscales.view(np.uint16))
+                assert np.array_equal(zeros, rzeros)
+
+
+def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g):
+    """The same method through the upper Cholesky factor U of H^-1 (H^-1 =
+    U^T U): err = (w_i - deq_i) / U_ii, w_j -= err * U_ij."""
+    N, K = w.shape
+    M = (1 << bits) - 1
+    U = np.linalg.cholesky(np.linalg.inv(H)).T
+    cur = w.astype(np.float64)
+    codes = np.zeros((N, K), np.uint8)
+    gs = K if g == 0 else g
+    for i in range(K):
+        s = scales[:, i // gs].astype(np.float64)
+        z = zeros[:, i // gs].astype(np.int64)
+        q = np.clip(np.rint(cur[:, i] / s).astype(np.int64) + z, 0, M)
+        codes[:, i] = q
+        deq = ((q - z) * s).astype(np.float16).astype(np.float64)
+        err = (cur[:, i] - deq) / U[i, i]
+        cur[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    return codes
+
+
+def _gptq_reverse_cholesky_form(w, H, scales, zeros, bits, g):
+    """The same method through R with H = R R^T, R upper triangular (the
+    Cholesky factor of H with the index order reversed), without an inverse:
+    t_j = w_j + (sum_{i<j} d_i R_ij) / R_jj with d_i = w_i - deq_i on the
+    ORIGINAL weights."""
+    N, K = w.shape
+    M = (1 << bits) - 1
+    P = np.eye(K)[::-1]
+    R = P @ np.linalg.cholesky(P @ H @ P) @ P
+    wf = w.astype(np.float64)
+    d = np.zeros((N, K))
+    codes = np.zeros((N, K), np.uint8)
+    gs = K if g == 0 else g
+    for j in range(K):
+        s = scales[:, j // gs].astype(np.float64)
+        z = zeros[:, j // gs].astype(np.int64)
+        t = wf[:, j] + d[:, :j] @ R[:j, j] / R[j, j]
+        q = np.clip(np.rint(t / s).astype(np.int64) + z, 0, M)
+        codes[:, j] = q
+        d[:, j] = wf[:, j] - ((q - z) * s).astype(np.float16).astype(np.float64)
+    return codes
+
+
+def check_gptq_other_formulations(o) -> None:
+    """Two algebraically equal formulations, written independently in numpy,
+    give the same codes on random correlated calibration data.  (They differ
+    from the oracle only by fp64 rounding; a code could flip only when a
+    quotient lands within ~1e-12 of a rounding midpoint.)"""
+    rng = np.random.default_rng(2323)
+    for trial in range(12):
+        K = (32, 48, 64)[trial % 3]
+        n = 3 * K
+        mix = rng.standard_normal((K, K)) / np.sqrt(K) + np.eye(K)
+        x = (rng.standard_normal((n, K)) @ mix).astype(np.float16)
+        H = o.hessian(x, 0.01)
+        w = (rng.standard_normal((5, K)) * rng.choice([0.02, 1.0])).astype(np.float16)
+        bits = (2, 3, 4, 8)[trial % 4]
+        g = (0, 16)[trial % 2]
+        codes, scales, zeros = o.quantize_gptq(w, H, bits, g)
+        s = scales.astype(np.float64)
+        assert np.array_equal(codes, _gptq_upper_cholesky_form(w, H, s, zeros, bits, g)), trial
+        assert np.array_equal(codes, _gptq_reverse_cholesky_form(w, H, s, zeros, bits, g)), trial
+
+
+def check_gptq_lowers_output_error(o) -> None:
+    """The point of the feedback: on correlated inputs the layer-output error
+    ||(W - deq(Q)) X^T|| is smaller than that of round-to-nearest."""
+    rng = np.random.default_rng(99)
+    K, n = 64, 256
+    mix = rng.standard_normal((K, K)) / np.sqrt(K) + np.eye(K)
+    x = (rng.standard_normal((n, K)) @ mix).astype(np.float16)
+    H = o.hessian(x, 0.01)
+    w = (rng.standard_normal((16, K)) * 0.02).astype(np.float16)
+    xf = x.astype(np.float64)
+    for bits in (2, 3, 4):
+        qg, s, z = o.quantize_gptq(w, H, bits, 0)
+        qr, _, _ = o.quantize_rtn(w, bits, 0)
+        dg = o.dequant(qg, s, z, bits, 0).astype(np.float64)
+        dr = o.dequant(qr, s, z, bits, 0).astype(np.float64)
+        wf = w.astype(np.float64)
+        eg = np.linalg.norm((wf - dg) @ xf.T)
+        er = np.linalg.norm((wf - dr) @ xf.T)
+        assert eg < er, (bits, eg, er)
+
+
+# ---------------------------------------------------------------------------
 # The reference product against exact integer arithmetic
 # ---------------------------------------------------------------------------
 def check_matmul_exact(o) -> None:
@@ -457,4 +597,7 @@ ALL_CHECKS = [check_sym_worked_examples, check_sym_invariants, check_sym_scale_i
               check_sym_bruteforce, check_f16_decode, check_f16_encode, check_worked_examples,
               check_pack_closed_forms, check_pack_bigint, check_invariants,
               check_scale_is_nearest, check_dequant_is_nearest, check_rtn_bruteforce,
-              check_matmul_exact, check_meta_words, check_meta_round_trip]
+              check_matmul_exact, check_meta_words, check_meta_round_trip,
+              check_gptq_worked_example, check_gptq_hessian_closed_form,
+              check_gptq_uncoupled_is_rtn, check_gptq_other_formulations,
+              check_gptq_lowers_output_error]

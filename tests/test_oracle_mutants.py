@@ -50,6 +50,15 @@ MUTANTS = {
     "meta_no_saturation": ("if (z > 32767) { z = 32767; ++saturated; }", ""),
     "meta_fields_swapped": ("meta[i] = (uint32_t)scales[i] | (zfield << 16);",
                             "meta[i] = zfield | ((uint32_t)scales[i] << 16);"),
+    "gptq_update_sign": ("for (int64_t j = i + 1; j < K; ++j) cur[n * K + j] -= err * hinv[i * K + j];",
+                         "for (int64_t j = i + 1; j < K; ++j) cur[n * K + j] += err * hinv[i * K + j];"),
+    "gptq_no_downdate": ("for (int64_t k = i + 1; k < K; ++k) hinv[j * K + k] -= f * hinv[i * K + k];",
+                         ""),
+    "gptq_err_not_scaled": ("const double err = (v - deq) / hii;", "const double err = (v - deq);"),
+    "hessian_damp_not_mean": ("const double add = damp * tr / (double)K;",
+                              "const double add = damp * tr;"),
+    "hessian_missing_factor_two": ("H[i * K + j] = 2.0 * acc / (double)n;",
+                                   "H[i * K + j] = acc / (double)n;"),
 }
 
 
