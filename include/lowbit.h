@@ -179,6 +179,40 @@ LOWBIT_API int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* p
                                  const uint32_t* meta, int64_t N, int64_t K, int bits,
                                  int64_t group_size, void* y_f16, void* hip_stream);
 
+/*
+ * Error-feedback quantization (GPTQ / OPTQ): the parameters of each output
+ * row are quantized one input channel after another, and the inverse of the
+ * Hessian built from the layer's input activations adjusts the parameters
+ * not yet quantized (BladeLLM model quantization, "Quantization algorithms",
+ * GPTQ; OPTQ reproducibility card, "Experiment Setup" row: Hessians from
+ * calibration inputs, per-row asymmetric min-max grid).  Contract:
+ *  - H = (2/n) X^T X over the calibration rows x_f16[n_samples][K] (fp16,
+ *    device), in fp64, plus damp * mean(diag H) on the diagonal (damp > 0;
+ *    0.01 is customary);
+ *  - scales and zeros are exactly those of lowbit_quantize_rtn on w (the
+ *    grid of the original weights, per row or per group);
+ *  - columns are taken in order 0..K-1; column i's code is
+ *    clamp(rint(t_i / s) + zero, 0, M) on the current fp64 weight t_i, its
+ *    dequantized value deq_i = fp16_rne((q - zero) * s), and the error
+ *    (t_i - deq_i) / Hinv_ii is fed into the later columns of the row through
+ *    row i of the inverse Hessian of the columns not yet quantized;
+ *  - outputs as lowbit_quantize_rtn (codes and/or packed words, scales,
+ *    zeros), same shape rules.
+ * The computation runs in fp64 in the caller's device workspace of at least
+ * lowbit_gptq_workspace_bytes(N, K) bytes (256-byte aligned; returns a
+ * negative status for invalid sizes).  On return of the work its first int32
+ * is 0, or 1 when H was not positive definite (all calibration inputs zero),
+ * in which case the codes are unspecified.  Calls on one workspace must not
+ * overlap.  The library allocates nothing.
+ */
+LOWBIT_API int64_t lowbit_gptq_workspace_bytes(int64_t N, int64_t K);
+LOWBIT_API int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                                    int64_t n_samples, double damp, int bits,
+                                    int64_t group_size, uint8_t* codes_or_null,
+                                    uint32_t* packed_or_null, uint16_t* scales_f16,
+                                    int32_t* zeros, void* workspace, int64_t workspace_bytes,
+                                    void* hip_stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 LOWBIT_API const char* lowbit_status_string(int status);
 

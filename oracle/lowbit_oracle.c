@@ -50,6 +50,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---------------------------------------------------------------------- */
@@ -303,13 +304,17 @@ int orc_unpack_meta(const uint32_t* meta, int64_t count, uint16_t* scales, int32
 /* damp * mean(diag H) on the diagonal (R17).                               */
 int orc_hessian(const uint16_t* x, int64_t n, int64_t K, double damp, double* H) {
     if (!x || !H || n <= 0 || K <= 0 || damp < 0) return -1;
-    for (int64_t i = 0; i < K; ++i)
-        for (int64_t j = 0; j < K; ++j) {
-            double acc = 0.0;
-            for (int64_t t = 0; t < n; ++t)
-                acc += orc_f16_to_f64(x[t * K + i]) * orc_f16_to_f64(x[t * K + j]);
-            H[i * K + j] = 2.0 * acc / (double)n;
-        }
+    double* row = (double*)malloc((size_t)K * sizeof(double));
+    if (!row) return -1;
+    /* acc[i][j] = sum over t (in order) of x[t][i] * x[t][j] */
+    for (int64_t i = 0; i < K * K; ++i) H[i] = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        for (int64_t i = 0; i < K; ++i) row[i] = orc_f16_to_f64(x[t * K + i]);
+        for (int64_t i = 0; i < K; ++i)
+            for (int64_t j = 0; j < K; ++j) H[i * K + j] += row[i] * row[j];
+    }
+    free(row);
+    for (int64_t i = 0; i < K * K; ++i) H[i] = 2.0 * H[i] / (double)n;
     double tr = 0.0;
     for (int64_t i = 0; i < K; ++i) tr += H[i * K + i];
     const double add = damp * tr / (double)K;
@@ -319,7 +324,9 @@ int orc_hessian(const uint16_t* x, int64_t n, int64_t K, double damp, double* H)
 
 /* Inverse of a symmetric positive definite matrix by Gauss-Jordan          */
 /* elimination on [A | I] (no pivoting: the pivots of an SPD matrix are      */
-/* positive).  Returns -1 on a non-positive pivot.                          */
+/* positive).  Before step c, columns < c of the left half are unit columns  */
+/* and row c of the right half is zero beyond column c, so the row updates   */
+/* skip those known zeros.  Returns -1 on a non-positive pivot.             */
 static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
     for (int64_t i = 0; i < K; ++i)
         for (int64_t j = 0; j < K; ++j) {
@@ -329,18 +336,14 @@ static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
     for (int64_t c = 0; c < K; ++c) {
         const double p = work[c * K + c];
         if (!(p > 0.0)) return -1;
-        for (int64_t j = 0; j < K; ++j) {
-            work[c * K + j] /= p;
-            inv[c * K + j] /= p;
-        }
+        for (int64_t j = c; j < K; ++j) work[c * K + j] /= p;
+        for (int64_t j = 0; j <= c; ++j) inv[c * K + j] /= p;
         for (int64_t r = 0; r < K; ++r) {
             if (r == c) continue;
             const double f = work[r * K + c];
             if (f == 0.0) continue;
-            for (int64_t j = 0; j < K; ++j) {
-                work[r * K + j] -= f * work[c * K + j];
-                inv[r * K + j] -= f * inv[c * K + j];
-            }
+            for (int64_t j = c; j < K; ++j) work[r * K + j] -= f * work[c * K + j];
+            for (int64_t j = 0; j <= c; ++j) inv[r * K + j] -= f * inv[c * K + j];
         }
     }
     return 0;
@@ -363,7 +366,7 @@ int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, 
     if (orc_quantize_rtn(w, N, K, bits, group_size, codes, scales, zeros) != 0) return -1;
     const int64_t g = group_size == 0 ? K : group_size;
     const int64_t G = groups_of(K, group_size);
-    const int M = (1 << bits) - 1;
+    const int64_t maxq = (1 << bits) - 1;
     double* hinv = work;
     double* tmp = work + K * K;
     double* cur = work + 3 * K * K;
@@ -379,7 +382,7 @@ int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, 
             const double v = cur[n * K + i];
             int64_t q = (int64_t)nearbyint(v / s) + z;
             if (q < 0) q = 0;
-            if (q > M) q = M;
+            if (q > maxq) q = maxq;
             codes[n * K + i] = (uint8_t)q;
             const double deq = orc_f16_to_f64(orc_f64_to_f16((double)(q - z) * s));
             const double err = (v - deq) / hii;

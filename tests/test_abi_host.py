@@ -31,8 +31,8 @@ def declared_entry_points():
 def test_header_declares_the_abi():
     assert declared_entry_points() == sorted(
         ["lowbit_pack", "lowbit_pack_meta", "lowbit_qgemm", "lowbit_qgemm_meta", "lowbit_qgemv",
-         "lowbit_qgemv_meta", "lowbit_quantize_rtn", "lowbit_quantize_rtn_sym",
-         "lowbit_status_string"])
+         "lowbit_qgemv_meta", "lowbit_quantize_gptq", "lowbit_quantize_rtn",
+         "lowbit_quantize_rtn_sym", "lowbit_gptq_workspace_bytes", "lowbit_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lw):
@@ -117,6 +117,23 @@ MIS = P + 4
     (lambda lw: lw.qgemv_meta_raw(P, 1, P, P, 4, 160, 4, 64, P, None), "SHAPE"),
     (lambda lw: lw.pack_meta_raw(None, None, 0, 4, None, None, None), "OK"),
     (lambda lw: lw.qgemm_meta_raw(None, 0, None, None, 4, 128, 4, 0, None, None), "OK"),
+    # error-feedback quantization (workspace of 1 MiB at a fake 256-aligned address)
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, P, 64, 0.01, 6, 0, P, P, P, P, P, 1 << 20, None),
+     "UNSUPPORTED"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 96, P, 64, 0.01, 4, 64, P, P, P, P, P, 1 << 20, None),
+     "SHAPE"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, P, 64, 0.0, 4, 0, P, P, P, P, P, 1 << 20, None),
+     "ARG"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, P, 0, 0.01, 4, 0, P, P, P, P, P, 1 << 20, None),
+     "ARG"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, P, 64, 0.01, 4, 0, P, P, P, P, P + 16, 1 << 20,
+                                     None), "ARG"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, P, 64, 0.01, 4, 0, P, P, P, P, P, 1024, None),
+     "ARG"),
+    (lambda lw: lw.quantize_gptq_raw(P, 4, 128, None, 64, 0.01, 4, 0, P, P, P, P, P, 1 << 20,
+                                     None), "ARG"),
+    (lambda lw: lw.quantize_gptq_raw(None, 0, 128, None, 64, 0.01, 4, 0, None, None, None, None,
+                                     None, 0, None), "OK"),
     # empty problems are valid and launch nothing
     (lambda lw: lw.quantize_rtn_raw(None, 0, 128, 4, 0, None, None, None, None, None), "OK"),
     (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),
@@ -134,3 +151,11 @@ def test_binding_refuses_cpu_tensors(lw):
     w = torch.zeros(4, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         lw.quantize_rtn(w, 4, 0)
+
+
+def test_gptq_workspace_size(lw):
+    K, N = 4096, 11008
+    up = lambda b: (b + 255) // 256 * 256
+    assert lw.gptq_workspace_bytes(N, K) == 256 + up(K * K * 8) + up(K * N * 8) + up(N * K)
+    assert lw.gptq_workspace_bytes(-1, K) < 0
+    assert lw.gptq_workspace_bytes(N, 0) < 0

@@ -1,0 +1,141 @@
+"""Error-feedback (GPTQ) quantization on the GPU (lowbit_quantize_gptq, fp64)
+against the oracle's inverse-Hessian formulation.
+
+Bar: codes, packed words, scales and zeros bit-exact.  Both sides decide every
+code in fp64; they compute the running weights in different (algebraically
+equal) ways, so a code could differ only where a quotient falls within about
+1e-12 of a rounding midpoint, which seeded continuous inputs do not produce.
+Shapes cover K that is not a multiple of the 64-column block, ragged row
+tiles, every width, per-row and grouped grids (power-of-two and other group
+sizes), and one workload layer at full size (rows sampled for the oracle).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import harness
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lw():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_bit_rtn_amd as lw
+    lw.load_library()
+    return lw
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _to_gpu(a):
+    import torch
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def _calibration(n: int, K: int, seed: int, correlated: bool) -> np.ndarray:
+    """Synthetic calibration inputs: N(0, 1), optionally mixed across channels
+    so that the Hessian has off-diagonal structure."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, K))
+    if correlated:
+        x = x @ (np.eye(K) + rng.standard_normal((K, K)) / np.sqrt(K))
+    return x.astype(np.float16)
+
+
+def _check(lw, w, x, bits, g, damp, what, codes=True, packed=True):
+    import torch
+    H = harness.oracle.hessian(x, damp)
+    rc, rs, rz = harness.oracle.quantize_gptq(w, H, bits, g)
+    out = lw.quantize_gptq(_to_gpu(w), _to_gpu(x), bits, g, damp, codes=codes, packed=packed)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0, f"{what}: Hessian reported not positive definite"
+    assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16), rs.view(np.uint16)), what
+    assert np.array_equal(out["zeros"].cpu().numpy(), rz), what
+    if codes:
+        got = out["codes"].cpu().numpy()
+        bad = np.argwhere(got != rc)
+        assert bad.size == 0, f"{what}: {len(bad)} codes differ, first {bad[:5].tolist()}"
+    if packed:
+        want = harness.oracle.pack(rc, bits)
+        assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), want), what
+    return rc
+
+
+CASES = [(5, 32, 4, 0), (17, 128, 3, 0), (64, 192, 2, 32), (67, 128, 4, 64), (130, 96, 8, 0),
+         (70, 160, 4, 32), (33, 352, 4, 0), (129, 512, 3, 128), (40, 480, 4, 96),
+         (21, 320, 2, 64), (66, 256, 8, 32)]
+
+
+@pytest.mark.parametrize("N,K,bits,g", CASES)
+@pytest.mark.parametrize("correlated", [False, True], ids=["iid", "mixed"])
+def test_gptq_matches_oracle(lw, N, K, bits, g, correlated):
+    _say(f"[gptq] N={N} K={K} bits={bits} g={g} correlated={correlated}")
+    rng = np.random.default_rng(N * 7 + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    x = _calibration(2 * K, K, seed=K + bits, correlated=correlated)
+    codes = _check(lw, w, x, bits, g, 0.01, f"N={N} K={K} bits={bits} g={g}")
+    if correlated:
+        rtn, _, _ = harness.oracle.quantize_rtn(w, bits, g)
+        assert (codes != rtn).any(), "error feedback changed no code"
+
+
+@pytest.mark.parametrize("want", [(True, False), (False, True)], ids=["codes", "packed"])
+def test_gptq_single_output(lw, want):
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((50, 128)) * 0.02).astype(np.float16)
+    x = _calibration(200, 128, seed=5, correlated=True)
+    _check(lw, w, x, 4, 32, 0.05, "single output", codes=want[0], packed=want[1])
+
+
+def test_gptq_degenerate_rows(lw):
+    """Constant, zero and one-signed rows, and few calibration samples (a
+    low-rank X^T X that only the damping makes positive definite)."""
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((20, 128)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[4] = 0.25
+    w[5] = np.abs(w[5]) + 1.0
+    w[6] *= 1e-3
+    x = _calibration(8, 128, seed=9, correlated=False)
+    for bits, g in ((2, 0), (4, 32), (8, 0)):
+        _check(lw, w.astype(np.float16), x, bits, g, 0.01, f"degenerate bits={bits} g={g}")
+
+
+def test_gptq_full_size_sampled(lw):
+    """The 2048 x 2048, 4-bit, groups-of-128 layer with its 1% outlier input
+    channels, 2048 calibration rows; the oracle checks 96 sampled rows (rows
+    are independent given the Hessian)."""
+    import torch
+    layer = [L for L in harness.all_layers() if L.name == "outlier_2048"][0]
+    _say(f"[gptq full size] {layer.name}")
+    w = layer.weights()
+    K = layer.K
+    cols = synth.outlier_columns(K, layer.outlier_frac, layer.seed)
+    xs = np.random.default_rng(11).standard_normal((2048, K))
+    xs[:, cols] *= layer.outlier_scale
+    x = xs.astype(np.float16)
+    out = lw.quantize_gptq(_to_gpu(w), _to_gpu(x), layer.bits, layer.group_size, 0.01)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    rows = harness.sample_rows(layer.N, 96, seed=3)
+    H = harness.oracle.hessian(x, 0.01)
+    rc, rs, rz = harness.oracle.quantize_gptq(w[rows], H, layer.bits, layer.group_size)
+    got = out["codes"].cpu().numpy()[rows]
+    bad = np.argwhere(got != rc)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+    assert np.array_equal(out["scales"].cpu().numpy()[rows].view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(out["zeros"].cpu().numpy()[rows], rz)
+    want = harness.oracle.pack(got, layer.bits)
+    assert np.array_equal(out["packed"].cpu().numpy()[rows].view(np.uint32), want)

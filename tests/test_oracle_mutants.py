@@ -57,8 +57,7 @@ MUTANTS = {
     "gptq_err_not_scaled": ("const double err = (v - deq) / hii;", "const double err = (v - deq);"),
     "hessian_damp_not_mean": ("const double add = damp * tr / (double)K;",
                               "const double add = damp * tr;"),
-    "hessian_missing_factor_two": ("H[i * K + j] = 2.0 * acc / (double)n;",
-                                   "H[i * K + j] = acc / (double)n;"),
+    "hessian_missing_factor_two": ("H[i] = 2.0 * H[i] / (double)n;", "H[i] = H[i] / (double)n;"),
 }
 
 

@@ -14,6 +14,7 @@ Functions mirror the C entry points:
   qgemm(x, packed, scales, zeros, K, bits, group_size) -> y      (any B)
   pack_meta(scales, zeros) -> (meta, saturated)                   compact group words
   qgemv_meta / qgemm_meta(x, packed, meta, K, bits, group_size) -> y
+  quantize_gptq(w, x_calib, bits, group_size, damp=0.01) -> dict   error-feedback codes
 """
 from __future__ import annotations
 
@@ -32,7 +33,8 @@ QGEMV_MAX_B = 15
 QUANTIZE_MAX_K = 131072
 
 EXPORTED = ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
-            "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta", "lowbit_status_string")
+            "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta", "lowbit_gptq_workspace_bytes",
+            "lowbit_quantize_gptq", "lowbit_status_string")
 
 _lib = None
 
@@ -59,10 +61,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowbit_qgemv.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_pack_meta.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.lowbit_gptq_workspace_bytes.argtypes = [i64, i64]
+    lib.lowbit_gptq_workspace_bytes.restype = i64
+    lib.lowbit_quantize_gptq.argtypes = [vp, i64, i64, vp, i64, ctypes.c_double, i32, i64, vp,
+                                         vp, vp, vp, vp, i64, vp]
     lib.lowbit_qgemv_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     for name in ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv",
-                 "lowbit_qgemm", "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta"):
+                 "lowbit_qgemm", "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta",
+                 "lowbit_quantize_gptq"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_status_string.restype = ctypes.c_char_p
@@ -275,3 +282,51 @@ def qgemm_meta(x, packed, meta, K: int, bits: int, group_size: int, out=None):
     """qgemm with compact group words."""
     return _product_meta(qgemm_meta_raw, "lowbit_qgemm_meta", x, packed, meta, K, bits,
                          group_size, out)
+
+
+def gptq_workspace_bytes(N: int, K: int) -> int:
+    return int(load_library().lowbit_gptq_workspace_bytes(N, K))
+
+
+def quantize_gptq_raw(w, N, K, x, n, damp, bits, group_size, codes, packed, scales, zeros,
+                      workspace, workspace_bytes, stream) -> int:
+    return load_library().lowbit_quantize_gptq(w, N, K, x, n, float(damp), bits, group_size,
+                                               codes, packed, scales, zeros, workspace,
+                                               workspace_bytes, stream)
+
+
+def quantize_gptq(w, x_calib, bits: int, group_size: int, damp: float = 0.01,
+                  codes: bool = True, packed: bool = True, workspace=None) -> dict:
+    """Error-feedback (GPTQ) quantization of fp16 w[N][K] with the Hessian of
+    the fp16 calibration rows x_calib[n][K], on the GPU in fp64.  Returns the
+    outputs of quantize_rtn plus ``status`` (device int32: 0, or 1 when the
+    Hessian was not positive definite).  ``workspace``: optional uint8 device
+    tensor of at least gptq_workspace_bytes(N, K) bytes."""
+    torch = _torch()
+    _require_gpu_tensor(w, "w", torch.float16)
+    _require_gpu_tensor(x_calib, "x_calib", torch.float16)
+    N, K = w.shape
+    if x_calib.dim() != 2 or x_calib.shape[1] != K:
+        raise ValueError("x_calib must be [n][K]")
+    G = groups(K, group_size)
+    dev = w.device
+    need = gptq_workspace_bytes(N, K)
+    if need < 0:
+        _check(need, "lowbit_gptq_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    off = (-workspace.data_ptr()) % 256
+    ws_ptr = workspace.data_ptr() + off
+    out = {"scales": torch.empty((N, G), dtype=torch.float16, device=dev),
+           "zeros": torch.empty((N, G), dtype=torch.int32, device=dev)}
+    if codes:
+        out["codes"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if packed:
+        out["packed"] = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=dev)
+    st = quantize_gptq_raw(w.data_ptr(), N, K, x_calib.data_ptr(), x_calib.shape[0], damp, bits,
+                           group_size, _ptr(out.get("codes")), _ptr(out.get("packed")),
+                           out["scales"].data_ptr(), out["zeros"].data_ptr(), ws_ptr,
+                           workspace.numel() - off, _stream_handle(dev))
+    _check(st, "lowbit_quantize_gptq")
+    out["status"] = workspace[off:off + 4].view(torch.int32)
+    return out

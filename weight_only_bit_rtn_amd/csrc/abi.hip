@@ -200,6 +200,38 @@ int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* packed, cons
       static_cast<hipStream_t>(hip_stream)));
 }
 
+int64_t lowbit_gptq_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K > LOWBIT_QUANTIZE_MAX_K || N > INT32_MAX) return LOWBIT_ERR_ARG;
+  return (int64_t)lowbit::gptq_workspace_bytes(N, K);
+}
+
+int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                         int64_t n_samples, double damp, int bits, int64_t group_size,
+                         uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                         int32_t* zeros, void* workspace, int64_t workspace_bytes,
+                         void* hip_stream) {
+  int rc = check_bits(bits);
+  if (rc != LOWBIT_OK) return rc;
+  rc = check_shape(N, K, bits, group_size);
+  if (rc != LOWBIT_OK) return rc;
+  if (K > LOWBIT_QUANTIZE_MAX_K || N > INT32_MAX) return LOWBIT_ERR_SHAPE;
+  if (!(damp > 0.0) || !(damp < 1e300) || n_samples <= 0) return LOWBIT_ERR_ARG;
+  if (N == 0) return LOWBIT_OK;
+  if (!w_f16 || !x_f16 || !scales_f16 || !zeros || !workspace ||
+      (!codes_or_null && !packed_or_null))
+    return LOWBIT_ERR_ARG;
+  if (!aligned16(w_f16) || !aligned16(x_f16) || !aligned16(scales_f16) || !aligned16(zeros) ||
+      (codes_or_null && !aligned16(codes_or_null)) ||
+      (packed_or_null && !aligned16(packed_or_null)) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return LOWBIT_ERR_ARG;
+  if (workspace_bytes < (int64_t)lowbit::gptq_workspace_bytes(N, K)) return LOWBIT_ERR_ARG;
+  return hip_status(lowbit::launch_gptq(
+      static_cast<const uint16_t*>(w_f16), N, K, static_cast<const uint16_t*>(x_f16), n_samples,
+      damp, bits, group_size, codes_or_null, packed_or_null, scales_f16, zeros, workspace,
+      static_cast<hipStream_t>(hip_stream)));
+}
+
 const char* lowbit_status_string(int status) {
   switch (status) {
     case LOWBIT_OK:

@@ -19,6 +19,14 @@ hipError_t launch_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uin
 hipError_t launch_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_t count,
                             uint32_t* meta, int32_t* saturated, hipStream_t stream);
 
+// Error-feedback (GPTQ) quantization in fp64; the workspace holds a status
+// word, the K x K Hessian factor, the K x N residuals and N x K codes.
+size_t gptq_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
+                       int64_t n_samples, double damp, int bits, int64_t group_size,
+                       uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
+                       void* workspace, hipStream_t stream);
+
 // The products take the group parameters as separate scales and zeros, or
 // (meta = true) as compact words passed through `scales` (zeros unused).
 
