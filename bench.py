@@ -21,7 +21,7 @@ separate stages.  The CPU baseline times the C oracle's dequantize + fp64
 product on a sample of rows of the same layers.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
-                       [--no-stages] [--only-gemv]
+                       [--no-stages] [--stage-reps 20] [--gptq-only] [--counter-pass]
 """
 from __future__ import annotations
 
@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix, published
+FP64_PEAK_TFLOPS = 78.6         # MI355X fp64 (vector and matrix), published
 MALL_DEFEAT_BYTES = 1 << 30
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "qgemv_opt175b_3bit_traffic.json")
 GEMV_SOURCES = ["gemv.hip", "gemv3.hip", "gemv_kernel.h", "unit_decode.h", "common.h"]
@@ -144,6 +145,55 @@ WIDE_LAYERS = (("opt175b_fc1_49152x12288_8bit", 49152, 12288, 8, 0, (1, 4)),
                ("llama70b_up_28672x8192_8bit", 28672, 8192, 8, 128, (16, 32, 64)))
 
 
+# Error-feedback (GPTQ) quantization, fp64: (layer name, calibration rows).
+GPTQ_LAYERS = (("outlier_2048", 2048), ("llama7b_up_11008x4096", 4096))
+
+
+def gptq_flops(N: int, K: int, n: int) -> float:
+    """fp64 operations of one call: the Hessian (2 n K^2, full matrix), its
+    Cholesky factor (K^3 / 3) and the feedback product (N K^2)."""
+    return 2.0 * n * K * K + K ** 3 / 3.0 + float(N) * K * K
+
+
+def measure_gptq(lw, torch, stream: int) -> dict:
+    import numpy as np
+    import synth
+    stages = {}
+    layers = {L.name: L for Ls in synth.WORKLOADS.values() for L in Ls}
+    dev = torch.device("cuda:0")
+    for name, n in GPTQ_LAYERS:
+        L = layers[name]
+        w = torch.from_numpy(L.weights()).to(dev)
+        x = torch.from_numpy(synth.normal_f16(n, L.K, 1.0, L.seed, synth.STREAM_X)).to(dev)
+        G = 1 if L.group_size == 0 else L.K // L.group_size
+        need = lw.gptq_workspace_bytes(L.N, L.K)
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+        off = (-ws.data_ptr()) % 256
+        packed = torch.empty((L.N, L.K * L.bits // 32), dtype=torch.int32, device=dev)
+        scales = torch.empty((L.N, G), dtype=torch.float16, device=dev)
+        zeros = torch.empty((L.N, G), dtype=torch.int32, device=dev)
+
+        def run(_):
+            st = lw.quantize_gptq_raw(w.data_ptr(), L.N, L.K, x.data_ptr(), n, 0.01, L.bits,
+                                      L.group_size, None, packed.data_ptr(), scales.data_ptr(),
+                                      zeros.data_ptr(), ws.data_ptr() + off, need, stream)
+            if st != 0:
+                raise RuntimeError(lw.status_string(st))
+
+        run(0)
+        avg, med, p10, p90 = time_launches(torch, run, 5, spread=True)
+        status = int(ws[off:off + 4].view(torch.int32).item())
+        fl = gptq_flops(L.N, L.K, n)
+        stages[f"gptq/{name}"] = {
+            "us": round(avg * 1e3, 1), "us_median": round(med * 1e3, 1),
+            "us_p10": round(p10 * 1e3, 1), "us_p90": round(p90 * 1e3, 1),
+            "calibration_rows": n, "fp64_flop": fl, "TFLOPs": round(fl / (avg * 1e-3) / 1e12, 2),
+            "fp64_frac": round(fl / (avg * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4), "status": status}
+        del w, x, ws, packed, scales, zeros
+        torch.cuda.empty_cache()
+    return stages
+
+
 def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     import synth
     stages = {}
@@ -210,6 +260,7 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
                 stages[f"{kern}/{layer.name}/B{B}"] = rec
             del prep
             torch.cuda.empty_cache()
+    stages.update(measure_gptq(lw, torch, stream))
     # a measured streaming reference next to the published peak: a plain
     # device-to-device copy (read + write) of 1 GiB
     src = torch.empty(COPY_REF_BYTES // 2, dtype=torch.float16, device="cuda:0").normal_()
@@ -325,6 +376,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--gptq-only", action="store_true",
+                    help="only the error-feedback (GPTQ) stages, printed as one JSON line")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for rocprofv3 --pmc: the quantizer and a few GEMV launches on both "
                          "layers, a few matrix-core launches of the Llama-70B MLP shape, then a "
@@ -334,7 +387,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the quantized GEMV path has no multi-GPU "
-              "component in this build (see the sharding notes in DESIGN.md); rerun with "
+              "component (it would shard by output rows, one row slice per GPU); rerun with "
               "--gpus 1", file=sys.stderr)
         return 2
 
@@ -349,6 +402,9 @@ def main() -> int:
     stream = torch.cuda.current_stream().cuda_stream
 
     layers = synth.WORKLOADS["opt175b_3bit"]
+    if args.gptq_only:
+        print(json.dumps({"gptq": measure_gptq(lw, torch, stream)}))
+        return 0
     if args.counter_pass:
         return counter_pass(lw, torch, layers, stream)
     footprint = sum(product_bytes(L.N, L.K, L.bits, L.group_size, 0) for L in layers)

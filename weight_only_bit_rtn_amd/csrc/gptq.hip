@@ -42,7 +42,8 @@ namespace {
 
 constexpr int kNB = 64;    // Cholesky panel width and GPTQ column block
 constexpr int kRows = 64;  // weight rows per GPTQ workgroup
-constexpr int kChunk = 32;  // earlier columns staged per LDS round in step 4
+constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
+constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
 
 __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
   return (double)__builtin_bit_cast(_Float16, b);
@@ -53,13 +54,13 @@ __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
 // Thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty.., columns 4 tx...
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                       int K, double* __restrict__ Hrev) {
-  __shared__ double xi[kChunk][64];
-  __shared__ double xj[kChunk][64];
+  __shared__ double xi[kHChunk][64];
+  __shared__ double xj[kHChunk][64];
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
   double acc[4][4] = {};
-  for (int64_t t0 = 0; t0 < n; t0 += kChunk) {
-    for (int e = tid; e < kChunk * 64; e += 256) {
+  for (int64_t t0 = 0; t0 < n; t0 += kHChunk) {
+    for (int e = tid; e < kHChunk * 64; e += 256) {
       const int tt = e >> 6, c = e & 63;
       const int64_t t = t0 + tt;
       xi[tt][c] = (t < n && i0 + c < K) ? h_bits_to_f64(x[t * K + i0 + c]) : 0.0;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
     }
     __syncthreads();
 #pragma unroll 4
-    for (int tt = 0; tt < kChunk; ++tt) {
+    for (int tt = 0; tt < kHChunk; ++tt) {
       double a[4], b[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -111,37 +112,41 @@ __global__ __launch_bounds__(1024) void damp_kernel(double* __restrict__ A, int 
 // Step 3a (one workgroup): Cholesky of the nb x nb diagonal block at kb.  A
 // non-positive pivot (H not positive definite) sets the status word and is
 // replaced by 1 so that the remaining steps stay finite.
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ A, int K, int kb,
-                                                        int nb, int32_t* __restrict__ status) {
-  __shared__ double a[kNB][kNB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < nb * nb; e += 256) {
-    const int r = e / nb, c = e % nb;
-    a[r][c] = A[(int64_t)(kb + r) * K + kb + c];
-  }
-  __syncthreads();
-  for (int c = 0; c < nb; ++c) {
-    if (tid == 0) {
-      double d = a[c][c];
+// One wave, lane r holding row r of the block in registers.  Step c: the
+// pivot comes from lane c, lanes below scale their entry of column c, the
+// column goes through LDS, and every lane updates its row (entries right of
+// its diagonal are never used).
+__global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ A, int K, int kb,
+                                                       int nb, int32_t* __restrict__ status) {
+  __shared__ double col[kNB];
+  const int r = threadIdx.x;
+  double a[kNB];
+#pragma unroll
+  for (int c = 0; c < kNB; ++c)
+    a[c] = (r < nb && c < nb) ? A[(int64_t)(kb + r) * K + kb + c] : (c == r ? 1.0 : 0.0);
+#pragma unroll
+  for (int c = 0; c < kNB; ++c) {
+    if (c < nb) {
+      double d = __shfl(a[c], c);
       if (!(d > 0.0)) {
-        status[0] = 1;
+        if (r == 0) status[0] = 1;
         d = 1.0;
       }
-      a[c][c] = __builtin_sqrt(d);
+      const double p = __builtin_sqrt(d);
+      const double lrc = r > c ? a[c] / p : (r == c ? p : a[c]);
+      a[c] = lrc;
+      col[r] = lrc;
+      __syncthreads();
+#pragma unroll
+      for (int k = c + 1; k < kNB; ++k)
+        if (r >= k) a[k] -= lrc * col[k];
+      __syncthreads();
     }
-    __syncthreads();
-    const int m = nb - c - 1;
-    if (tid < m) a[c + 1 + tid][c] /= a[c][c];
-    __syncthreads();
-    for (int e = tid; e < m * m; e += 256) {
-      const int r = c + 1 + e / m, k = c + 1 + e % m;
-      if (k <= r) a[r][k] -= a[r][c] * a[k][c];
-    }
-    __syncthreads();
   }
-  for (int e = tid; e < nb * nb; e += 256) {
-    const int r = e / nb, c = e % nb;
-    if (c <= r) A[(int64_t)(kb + r) * K + kb + c] = a[r][c];
+  if (r < nb) {
+#pragma unroll
+    for (int c = 0; c < kNB; ++c)
+      if (c <= r) A[(int64_t)(kb + r) * K + kb + c] = a[c];
   }
 }
 
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int G, int gsz,
     int M, double* __restrict__ DT, uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
+  __shared__ double dsm[kChunk][kRows];     // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][kRows];         // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 1];       // R[jb + a][jb + c], the block's own rows
   __shared__ uint16_t ws[kRows][kNB + 2];   // the block's original weights
@@ -238,26 +244,51 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
 
   for (int jb = 0; jb < K; jb += kNB) {
     const int nb = min(kNB, K - jb);
-    // contribution of the columns before the block: 16 block columns per wave
-    double acc[16];
+    // contribution of the columns before the block: thread (ty, tx) sums
+    // rows 4 ty .. 4 ty + 3 and block columns 4 tx .. 4 tx + 3
+    const int ty = tid >> 4, tx = tid & 15;
+    double acc[4][4] = {};
+    // Chunks of 64 earlier columns: R rows and residuals staged in LDS, the
+    // next chunk's loads issued (into registers) before this chunk's products.
+    const int nchunks = jb / kChunk;
+    double pr[16], pd[16];
+    auto fetch = [&](int i0) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = 0.0;
-    for (int i0 = 0; i0 < jb; i0 += kChunk) {
-      for (int e = tid; e < kChunk * kNB; e += 256) {
-        const int ii = e / kNB, c = e % kNB;
-        rs[ii][c] = c < nb ? Rat(i0 + ii, jb + c) : 0.0;
+      for (int k = 0; k < 16; ++k) {
+        const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
+        pr[k] = c < nb ? Rat(i0 + ii, jb + c) : 0.0;
+        pd[k] = r0 + c < N ? DT[(int64_t)(i0 + ii) * N + r0 + c] : 0.0;
+      }
+    };
+    if (nchunks > 0) fetch(0);
+    for (int ch = 0; ch < nchunks; ++ch) {
+      __syncthreads();  // the previous chunk has been read
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
+        rs[ii][c] = pr[k];
+        dsm[ii][c] = pd[k];
       }
       __syncthreads();
+      if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
 #pragma unroll 4
       for (int ii = 0; ii < kChunk; ++ii) {
-        const double dv = valid ? DT[(int64_t)(i0 + ii) * N + row] : 0.0;
+        double a[4], b[4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[c] = __builtin_fma(dv, rs[ii][16 * wave + c], acc[c]);
+        for (int u = 0; u < 4; ++u) {
+          a[u] = dsm[ii][4 * ty + u];
+          b[u] = rs[ii][4 * tx + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
       }
-      __syncthreads();
     }
 #pragma unroll
-    for (int c = 0; c < 16; ++c) cs[16 * wave + c][lane] = acc[c];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cs[4 * tx + v][4 * ty + u] = acc[u][v];
     for (int e = tid; e < kNB * kNB; e += 256) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
@@ -267,22 +298,37 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       ws[rr][c] = (r0 + rr < N && c < nb) ? w[(int64_t)(r0 + rr) * K + jb + c] : (uint16_t)0;
     }
     __syncthreads();
-    // the block's columns in order, one lane per row
+    // the block's columns in order, one lane per row; the row's running
+    // sums for the block's columns stay in registers
     if (wave == 0) {
-      for (int j = 0; j < nb; ++j) {
-        const int col = jb + j;
-        const int g = col / gsz;
-        const double s = valid ? h_bits_to_f64(scales[(int64_t)row * G + g]) : 1.0;
-        const int64_t z = valid ? zeros[(int64_t)row * G + g] : 0;
-        const double wv = h_bits_to_f64(ws[lane][j]);
-        const double t = wv + cs[j][lane] / rb[j][j];
-        int64_t q = (int64_t)__builtin_rint(t / s) + z;
-        q = q < 0 ? 0 : (q > M ? M : q);
-        const double deq = h_bits_to_f64(f64_to_h_bits((double)(q - z) * s));
-        const double d = wv - deq;
-        reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
-        if (valid) DT[(int64_t)col * N + row] = d;
-        for (int j2 = j + 1; j2 < nb; ++j2) cs[j2][lane] = __builtin_fma(d, rb[j][j2], cs[j2][lane]);
+      // a 64-column block meets at most two groups (groups are multiples of
+      // 32 columns, blocks start on multiples of 64)
+      const int g0 = jb / gsz, g1 = min((jb + nb - 1) / gsz, G - 1);
+      const double s0 = valid ? h_bits_to_f64(scales[(int64_t)row * G + g0]) : 1.0;
+      const double s1 = valid ? h_bits_to_f64(scales[(int64_t)row * G + g1]) : 1.0;
+      const int64_t z0 = valid ? zeros[(int64_t)row * G + g0] : 0;
+      const int64_t z1 = valid ? zeros[(int64_t)row * G + g1] : 0;
+      double cb[kNB];
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) cb[j] = cs[j][lane];
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) {
+        if (j < nb) {
+          const int col = jb + j;
+          const bool first = col / gsz == g0;
+          const double s = first ? s0 : s1;
+          const int64_t z = first ? z0 : z1;
+          const double wv = h_bits_to_f64(ws[lane][j]);
+          const double t = wv + cb[j] / rb[j][j];
+          int64_t q = (int64_t)__builtin_rint(t / s) + z;
+          q = q < 0 ? 0 : (q > M ? M : q);
+          const double deq = h_bits_to_f64(f64_to_h_bits((double)(q - z) * s));
+          const double d = wv - deq;
+          reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
+          if (valid) DT[(int64_t)col * N + row] = d;
+#pragma unroll
+          for (int j2 = j + 1; j2 < kNB; ++j2) cb[j2] = __builtin_fma(d, rb[j][j2], cb[j2]);
+        }
       }
     }
     __syncthreads();
@@ -325,7 +371,7 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, A, k, damp, status);
   for (int kb = 0; kb < k; kb += kNB) {
     const int nb = k - kb < kNB ? k - kb : kNB;
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, A, k, kb, nb, status);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, stream, A, k, kb, nb, status);
     const int below = k - kb - nb;
     if (below > 0) {
       hipLaunchKernelGGL(chol_panel_kernel, dim3((below + 255) / 256), dim3(256), 0, stream, A,
