@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <set>
+#include <utility>
 
 #include "../../include/lowbit.h"
 #include "common.h"
@@ -42,6 +44,19 @@ size_t device_lds_per_block() {
     cache[dev] = (size_t)v;
   }
   return cache[dev];
+}
+
+hipError_t raise_lds_limit(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;  // (kernel, device)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
 }
 
 }  // namespace lowbit

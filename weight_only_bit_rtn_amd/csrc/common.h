@@ -98,4 +98,9 @@ int device_cu_count();
 // device (bytes, cached per device).
 size_t device_lds_per_block();
 
+// Host side: allow `kernel` dynamic LDS allocations of up to `bytes` on the
+// current device (hipFuncSetAttribute), once per kernel and device; safe to
+// call from several host threads.
+hipError_t raise_lds_limit(const void* kernel, int bytes);
+
 }  // namespace lowbit

@@ -473,15 +473,8 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
   if (lds > device_lds_per_block()) return hipErrorNotSupported;
   const auto kern = qgemm_kernel<BITS, BT, GM, META>;
   // the LDS request exceeds the default limit: raise it once per device
-  static int raised[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!raised[dev]) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised[dev] = 1;
-  }
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), (int)lds);
+  if (e != hipSuccess) return e;
   const int NG = (N + 15) / 16;
   const int cus = device_cu_count();
   const int grid = NG < cus ? NG : cus;

@@ -603,16 +603,9 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   if (lds > 64 * 1024) {
     // above the default limit: raise it (once per device) to the largest
     // request this kernel can make
-    static int raised[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!raised[dev]) {
-      const int cap = (int)(device_lds_per_block() < kLdsBudget ? device_lds_per_block() : kLdsBudget);
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-      if (e != hipSuccess) return e;
-      raised[dev] = 1;
-    }
+    const int cap = (int)(device_lds_per_block() < kLdsBudget ? device_lds_per_block() : kLdsBudget);
+    const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), cap);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(kThreads), lds, stream, x, packed, scales, zeros, y, N,
                      K, G, gsz, gshift, J, lgjc, RT);
