@@ -170,10 +170,11 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A,
 #pragma unroll
   for (int c = 0; c < kNB; ++c) {
     if (c < nb) {
-      double s = v[c];
+      // four partial sums: a quarter of the dependent chain
+      double s4[4] = {v[c], 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int k = 0; k < c; ++k) s -= v[k] * l[c][k];
-      v[c] = s / l[c][c];
+      for (int k = 0; k < c; ++k) s4[k & 3] -= v[k] * l[c][k];
+      v[c] = ((s4[0] + s4[1]) + (s4[2] + s4[3])) / l[c][c];
     }
   }
 #pragma unroll
@@ -271,18 +272,27 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       }
       __syncthreads();
       if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
-#pragma unroll 4
-      for (int ii = 0; ii < kChunk; ++ii) {
-        double a[4], b[4];
+      // operands of step ii + 1 are read while step ii multiplies
+      double a[2][4], b[2][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[u] = dsm[ii][4 * ty + u];
-          b[u] = rs[ii][4 * tx + u];
+      for (int u = 0; u < 4; ++u) {
+        a[0][u] = dsm[0][4 * ty + u];
+        b[0][u] = rs[0][4 * tx + u];
+      }
+#pragma unroll
+      for (int ii = 0; ii < kChunk; ++ii) {
+        const int cur = ii & 1, nxt = cur ^ 1;
+        if (ii + 1 < kChunk) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            a[nxt][u] = dsm[ii + 1][4 * ty + u];
+            b[nxt][u] = rs[ii + 1][4 * tx + u];
+          }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+          for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[cur][u], b[cur][v], acc[u][v]);
       }
     }
 #pragma unroll
@@ -322,7 +332,14 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           const double t = wv + cb[j] / rb[j][j];
           int64_t q = (int64_t)__builtin_rint(t / s) + z;
           q = q < 0 ? 0 : (q > M ? M : q);
-          const double deq = h_bits_to_f64(f64_to_h_bits((double)(q - z) * s));
+          // (q - z) * s is exact in fp64; below 2^13 in magnitude |q - z| it
+          // has at most 24 significant bits, so the fp32 step is exact and
+          // the fp16 conversion is the only rounding
+          const int64_t qz = q - z;
+          const double prod = (double)qz * s;
+          const double deq = (qz > -8192 && qz < 8192)
+                                 ? (double)(_Float16)(float)prod
+                                 : h_bits_to_f64(f64_to_h_bits(prod));
           const double d = wv - deq;
           reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
           if (valid) DT[(int64_t)col * N + row] = d;
