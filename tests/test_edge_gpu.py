@@ -309,3 +309,31 @@ def test_error_returns_on_gpu(lw):
     assert lw.quantize_rtn_raw(p, 8, 128, 4, 0, None, None, p, p, stream) == lw.LOWBIT_ERR_ARG
     torch.cuda.synchronize()
     assert int(buf.abs().sum()) == 0
+
+
+def test_calls_follow_the_callers_stream(lw):
+    """Every entry point enqueues on the stream it is given (here a
+    side stream of default priority): results match the default-stream ones,
+    and work queued behind an event on that stream sees the outputs."""
+    import torch
+    N, K, bits, g = 257, 2048, 4, 128
+    w = _weights("normal", N, K, 3)
+    x = _to_gpu(harness.synth.normal_f16(4, K, 1.0, 0, 2))
+    ref = lw.quantize_rtn(_to_gpu(w), bits, g)
+    y_ref = lw.qgemv(x, ref["packed"], ref["scales"], ref["zeros"], K, bits, g)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    wg = _to_gpu(w)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q = lw.quantize_rtn(wg, bits, g)
+        y = lw.qgemv(x, q["packed"], q["scales"], q["zeros"], K, bits, g)
+        y2 = lw.qgemm(x, q["packed"], q["scales"], q["zeros"], K, bits, g)
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    assert torch.equal(q["packed"], ref["packed"])
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    y_host = harness.oracle_y(x.cpu().numpy(), ref["packed"].cpu().numpy().view(np.uint32),
+                              ref["scales"].cpu().numpy(), ref["zeros"].cpu().numpy(), K, bits, g)
+    harness.assert_y_close(y2.cpu().numpy(), y_host, "qgemm on a side stream")
