@@ -67,6 +67,8 @@ class Oracle:
         lib.orc_hessian.restype = ctypes.c_int
         lib.orc_quantize_gptq.argtypes = [vp, i64, i64, vp, i32, i64, vp, vp, vp, vp]
         lib.orc_quantize_gptq.restype = ctypes.c_int
+        lib.orc_quantize_gptq_sym.argtypes = [vp, i64, i64, vp, i32, i64, vp, vp, vp, vp]
+        lib.orc_quantize_gptq_sym.restype = ctypes.c_int
         for name in ("orc_quantize_rtn", "orc_quantize_rtn_sym", "orc_pack", "orc_unpack",
                      "orc_dequant", "orc_matmul_f64"):
             getattr(lib, name).restype = ctypes.c_int
@@ -131,9 +133,11 @@ class Oracle:
         _ok(self.lib.orc_hessian(xb.ctypes.data, n, K, float(damp), H.ctypes.data), "hessian")
         return H
 
-    def quantize_gptq(self, w: np.ndarray, H: np.ndarray, bits: int, group_size: int):
-        """Error-feedback codes of fp16 w[N][K] on the RTN grid of w, with the
-        Hessian H[K][K]; returns (codes, scales, zeros) as quantize_rtn."""
+    def quantize_gptq(self, w: np.ndarray, H: np.ndarray, bits: int, group_size: int,
+                      symmetric: bool = False):
+        """Error-feedback codes of fp16 w[N][K] on the RTN grid of w (min-max,
+        or signed symmetric), with the Hessian H[K][K]; returns (codes,
+        scales, zeros) as quantize_rtn."""
         wb = _bits16(w)
         N, K = wb.shape
         Hc = np.ascontiguousarray(H, dtype=np.float64)
@@ -143,9 +147,9 @@ class Oracle:
         scales = np.empty((N, G), np.uint16)
         zeros = np.empty((N, G), np.int32)
         work = np.empty(3 * K * K + N * K, np.float64)
-        _ok(self.lib.orc_quantize_gptq(wb.ctypes.data, N, K, Hc.ctypes.data, bits, group_size,
-                                       codes.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
-                                       work.ctypes.data), "quantize_gptq")
+        fn = self.lib.orc_quantize_gptq_sym if symmetric else self.lib.orc_quantize_gptq
+        _ok(fn(wb.ctypes.data, N, K, Hc.ctypes.data, bits, group_size, codes.ctypes.data,
+               scales.ctypes.data, zeros.ctypes.data, work.ctypes.data), "quantize_gptq")
         return codes, scales.view(np.float16), zeros
 
     def pack_meta(self, scales: np.ndarray, zeros: np.ndarray):
@@ -226,8 +230,8 @@ def hessian(x, damp):
     return default().hessian(x, damp)
 
 
-def quantize_gptq(w, H, bits, group_size):
-    return default().quantize_gptq(w, H, bits, group_size)
+def quantize_gptq(w, H, bits, group_size, symmetric=False):
+    return default().quantize_gptq(w, H, bits, group_size, symmetric)
 
 
 def f16_to_f64(h):

@@ -350,8 +350,9 @@ static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
 }
 
 /* GPTQ codes for w[N][K] given the Hessian H[K][K] (R18-R20):               */
-/*  - the grid (scales, zeros) is the min-max RTN grid of the ORIGINAL       */
-/*    weights, per row or per group, exactly as orc_quantize_rtn;           */
+/*  - the grid (scales, zeros) is the RTN grid of the ORIGINAL weights, per  */
+/*    row or per group, exactly as orc_quantize_rtn (min-max) or            */
+/*    orc_quantize_rtn_sym (signed symmetric, codes from 1);                */
 /*  - columns are taken in their natural order i = 0 .. K-1;                */
 /*  - at column i, with Hinv the inverse Hessian of the columns not yet      */
 /*    quantized: q = clamp(rint(w_i / s) + z, 0, M) on the current fp64     */
@@ -359,11 +360,14 @@ static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
 /*    w_j -= err * Hinv[i][j] for every later column j, then column i is     */
 /*    removed from Hinv: Hinv[j][k] -= Hinv[j][i] * Hinv[i][k] / Hinv[i][i]. */
 /* Rows are independent, so any subset of rows may be passed.              */
-int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
-                      int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
-                      double* work /* 3*K*K + N*K doubles */) {
+static int gptq_codes(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                      int64_t group_size, int sym, uint8_t* codes, uint16_t* scales,
+                      int32_t* zeros, double* work /* 3*K*K + N*K doubles */) {
     if (!w || !H || !codes || !scales || !zeros || !work || N < 0 || K <= 0) return -1;
-    if (orc_quantize_rtn(w, N, K, bits, group_size, codes, scales, zeros) != 0) return -1;
+    const int grid = sym ? orc_quantize_rtn_sym(w, N, K, bits, group_size, codes, scales, zeros)
+                         : orc_quantize_rtn(w, N, K, bits, group_size, codes, scales, zeros);
+    if (grid != 0) return -1;
+    const int64_t minq = sym ? 1 : 0;
     const int64_t g = group_size == 0 ? K : group_size;
     const int64_t G = groups_of(K, group_size);
     const int64_t maxq = (1 << bits) - 1;
@@ -381,7 +385,7 @@ int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, 
             const int64_t z = zeros[n * G + i / g];
             const double v = cur[n * K + i];
             int64_t q = (int64_t)nearbyint(v / s) + z;
-            if (q < 0) q = 0;
+            if (q < minq) q = minq;
             if (q > maxq) q = maxq;
             codes[n * K + i] = (uint8_t)q;
             const double deq = orc_f16_to_f64(orc_f64_to_f16((double)(q - z) * s));
@@ -395,6 +399,18 @@ int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, 
         }
     }
     return 0;
+}
+
+int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                      int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
+                      double* work) {
+    return gptq_codes(w, N, K, H, bits, group_size, 0, codes, scales, zeros, work);
+}
+
+int orc_quantize_gptq_sym(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                          int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
+                          double* work) {
+    return gptq_codes(w, N, K, H, bits, group_size, 1, codes, scales, zeros, work);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -54,6 +54,10 @@ int orc_hessian(const uint16_t* x, int64_t n, int64_t K, double damp, double* H)
 int orc_quantize_gptq(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
                       int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
                       double* work);
+/* The same on the signed symmetric grid of orc_quantize_rtn_sym (codes from 1). */
+int orc_quantize_gptq_sym(const uint16_t* w, int64_t N, int64_t K, const double* H, int bits,
+                          int64_t group_size, uint8_t* codes, uint16_t* scales, int32_t* zeros,
+                          double* work);
 
 #ifdef __cplusplus
 }

@@ -475,12 +475,17 @@ def check_gptq_uncoupled_is_rtn(o) -> None:
             for g in (0, 16, 32):
                 codes, scales, zeros = o.quantize_gptq(w, H, bits, g)
                 rcodes, rscales, rzeros = o.quantize_rtn(w, bits, g)
+                scodes, sscales, szeros = o.quantize_gptq(w, H, bits, g, symmetric=True)
+                rs = o.quantize_rtn_sym(w, bits, g)
+                assert np.array_equal(scodes, rs[0]), (trial, bits, g, "sym")
+                assert np.array_equal(sscales.view(np.uint16), rs[1].view(np.uint16))
+                assert np.array_equal(szeros, rs[2])
                 assert np.array_equal(codes, rcodes), (trial, bits, g)
                 assert np.array_equal(scales.view(np.uint16), rscales.view(np.uint16))
                 assert np.array_equal(zeros, rzeros)
 
 
-def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g):
+def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g, qlo=0):
     """The same method through the upper Cholesky factor U of H^-1 (H^-1 =
     U^T U): err = (w_i - deq_i) / U_ii, w_j -= err * U_ij."""
     N, K = w.shape
@@ -492,7 +497,7 @@ def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g):
     for i in range(K):
         s = scales[:, i // gs].astype(np.float64)
         z = zeros[:, i // gs].astype(np.int64)
-        q = np.clip(np.rint(cur[:, i] / s).astype(np.int64) + z, 0, M)
+        q = np.clip(np.rint(cur[:, i] / s).astype(np.int64) + z, qlo, M)
         codes[:, i] = q
         deq = ((q - z) * s).astype(np.float16).astype(np.float64)
         err = (cur[:, i] - deq) / U[i, i]
@@ -500,7 +505,7 @@ def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g):
     return codes
 
 
-def _gptq_reverse_cholesky_form(w, H, scales, zeros, bits, g):
+def _gptq_reverse_cholesky_form(w, H, scales, zeros, bits, g, qlo=0):
     """The same method through R with H = R R^T, R upper triangular (the
     Cholesky factor of H with the index order reversed), without an inverse:
     t_j = w_j + (sum_{i<j} d_i R_ij) / R_jj with d_i = w_i - deq_i on the
@@ -517,7 +522,7 @@ def _gptq_reverse_cholesky_form(w, H, scales, zeros, bits, g):
         s = scales[:, j // gs].astype(np.float64)
         z = zeros[:, j // gs].astype(np.int64)
         t = wf[:, j] + d[:, :j] @ R[:j, j] / R[j, j]
-        q = np.clip(np.rint(t / s).astype(np.int64) + z, 0, M)
+        q = np.clip(np.rint(t / s).astype(np.int64) + z, qlo, M)
         codes[:, j] = q
         d[:, j] = wf[:, j] - ((q - z) * s).astype(np.float16).astype(np.float64)
     return codes
@@ -538,10 +543,14 @@ def check_gptq_other_formulations(o) -> None:
         w = (rng.standard_normal((5, K)) * rng.choice([0.02, 1.0])).astype(np.float16)
         bits = (2, 3, 4, 8)[trial % 4]
         g = (0, 16)[trial % 2]
-        codes, scales, zeros = o.quantize_gptq(w, H, bits, g)
+        sym = trial % 3 == 2
+        codes, scales, zeros = o.quantize_gptq(w, H, bits, g, symmetric=sym)
+        qlo = 1 if sym else 0
+        if sym:
+            assert (zeros == 1 << (bits - 1)).all() and codes.min() >= 1, trial
         s = scales.astype(np.float64)
-        assert np.array_equal(codes, _gptq_upper_cholesky_form(w, H, s, zeros, bits, g)), trial
-        assert np.array_equal(codes, _gptq_reverse_cholesky_form(w, H, s, zeros, bits, g)), trial
+        assert np.array_equal(codes, _gptq_upper_cholesky_form(w, H, s, zeros, bits, g, qlo)), trial
+        assert np.array_equal(codes, _gptq_reverse_cholesky_form(w, H, s, zeros, bits, g, qlo)), trial
 
 
 def check_gptq_lowers_output_error(o) -> None:

@@ -55,6 +55,7 @@ MUTANTS = {
     "gptq_no_downdate": ("for (int64_t k = i + 1; k < K; ++k) hinv[j * K + k] -= f * hinv[i * K + k];",
                          ""),
     "gptq_err_not_scaled": ("const double err = (v - deq) / hii;", "const double err = (v - deq);"),
+    "gptq_sym_clamp_from_zero": ("const int64_t minq = sym ? 1 : 0;", "const int64_t minq = 0;"),
     "hessian_damp_not_mean": ("const double add = damp * tr / (double)K;",
                               "const double add = damp * tr;"),
     "hessian_missing_factor_two": ("H[i] = 2.0 * H[i] / (double)n;", "H[i] = H[i] / (double)n;"),
