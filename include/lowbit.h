@@ -213,6 +213,23 @@ LOWBIT_API int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, con
                                     int32_t* zeros, void* workspace, int64_t workspace_bytes,
                                     void* hip_stream);
 
+/*
+ * lowbit_quantize_gptq on the signed symmetric grid of
+ * lowbit_quantize_rtn_sym (BladeLLM model quantization, "Quantization modes":
+ * the weight-only mode lists gptq among its algorithms and quantizes on the
+ * signed symmetric grid unless told otherwise).  scales
+ * and zeros are exactly those of lowbit_quantize_rtn_sym on w (every zero is
+ * 2^(bits-1)); column i's code is clamp(rint(t_i / s) + zero, 1, M), so codes
+ * lie in [1, M] as there.  Everything else, including the workspace and the
+ * status word, exactly as lowbit_quantize_gptq.
+ */
+LOWBIT_API int lowbit_quantize_gptq_sym(const void* w_f16, int64_t N, int64_t K,
+                                        const void* x_f16, int64_t n_samples, double damp,
+                                        int bits, int64_t group_size, uint8_t* codes_or_null,
+                                        uint32_t* packed_or_null, uint16_t* scales_f16,
+                                        int32_t* zeros, void* workspace,
+                                        int64_t workspace_bytes, void* hip_stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 LOWBIT_API const char* lowbit_status_string(int status);
 

@@ -31,7 +31,8 @@ def declared_entry_points():
 def test_header_declares_the_abi():
     assert declared_entry_points() == sorted(
         ["lowbit_pack", "lowbit_pack_meta", "lowbit_qgemm", "lowbit_qgemm_meta", "lowbit_qgemv",
-         "lowbit_qgemv_meta", "lowbit_quantize_gptq", "lowbit_quantize_rtn",
+         "lowbit_qgemv_meta", "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym",
+         "lowbit_quantize_rtn",
          "lowbit_quantize_rtn_sym", "lowbit_gptq_workspace_bytes", "lowbit_status_string"])
 
 
@@ -134,6 +135,14 @@ MIS = P + 4
                                      None), "ARG"),
     (lambda lw: lw.quantize_gptq_raw(None, 0, 128, None, 64, 0.01, 4, 0, None, None, None, None,
                                      None, 0, None), "OK"),
+    (lambda lw: lw.quantize_gptq_sym_raw(P, 4, 128, P, 64, 0.01, 5, 0, P, P, P, P, P, 1 << 20,
+                                         None), "UNSUPPORTED"),
+    (lambda lw: lw.quantize_gptq_sym_raw(P, 4, 128, P, 64, -1.0, 4, 0, P, P, P, P, P, 1 << 20,
+                                         None), "ARG"),
+    (lambda lw: lw.quantize_gptq_sym_raw(P, 4, 128, P, 64, 0.01, 4, 0, P, P, P, P, P, 1024,
+                                         None), "ARG"),
+    (lambda lw: lw.quantize_gptq_sym_raw(None, 0, 128, None, 64, 0.01, 4, 0, None, None, None,
+                                         None, None, 0, None), "OK"),
     # empty problems are valid and launch nothing
     (lambda lw: lw.quantize_rtn_raw(None, 0, 128, 4, 0, None, None, None, None, None), "OK"),
     (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),

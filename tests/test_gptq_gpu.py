@@ -54,11 +54,12 @@ def _calibration(n: int, K: int, seed: int, correlated: bool) -> np.ndarray:
     return x.astype(np.float16)
 
 
-def _check(lw, w, x, bits, g, damp, what, codes=True, packed=True):
+def _check(lw, w, x, bits, g, damp, what, codes=True, packed=True, symmetric=False):
     import torch
     H = harness.oracle.hessian(x, damp)
-    rc, rs, rz = harness.oracle.quantize_gptq(w, H, bits, g)
-    out = lw.quantize_gptq(_to_gpu(w), _to_gpu(x), bits, g, damp, codes=codes, packed=packed)
+    rc, rs, rz = harness.oracle.quantize_gptq(w, H, bits, g, symmetric=symmetric)
+    out = lw.quantize_gptq(_to_gpu(w), _to_gpu(x), bits, g, damp, codes=codes, packed=packed,
+                           symmetric=symmetric)
     torch.cuda.synchronize()
     assert int(out["status"].item()) == 0, f"{what}: Hessian reported not positive definite"
     assert np.array_equal(out["scales"].cpu().numpy().view(np.uint16), rs.view(np.uint16)), what
@@ -111,6 +112,36 @@ def test_gptq_degenerate_rows(lw):
     x = _calibration(8, 128, seed=9, correlated=False)
     for bits, g in ((2, 0), (4, 32), (8, 0)):
         _check(lw, w.astype(np.float16), x, bits, g, 0.01, f"degenerate bits={bits} g={g}")
+
+
+SYM_CASES = [(5, 32, 4, 0), (17, 128, 3, 0), (64, 192, 2, 32), (67, 128, 4, 64),
+             (130, 96, 8, 0), (40, 480, 4, 96), (66, 256, 8, 32)]
+
+
+@pytest.mark.parametrize("N,K,bits,g", SYM_CASES)
+def test_gptq_symmetric_matches_oracle(lw, N, K, bits, g):
+    """lowbit_quantize_gptq_sym: the signed symmetric grid, codes in [1, M]."""
+    _say(f"[gptq sym] N={N} K={K} bits={bits} g={g}")
+    rng = np.random.default_rng(N * 5 + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    x = _calibration(2 * K, K, seed=K + bits + 1, correlated=True)
+    codes = _check(lw, w, x, bits, g, 0.01, f"sym N={N} K={K} bits={bits} g={g}",
+                   symmetric=True)
+    assert codes.min() >= 1
+    rtn, _, _ = harness.oracle.quantize_rtn_sym(w, bits, g)
+    assert (codes != rtn).any(), "error feedback changed no code"
+
+
+def test_gptq_symmetric_degenerate_rows(lw):
+    rng = np.random.default_rng(19)
+    w = (rng.standard_normal((12, 128)) * 0.02).astype(np.float32)
+    w[2] = 0.0
+    w[3] = -0.5
+    w[4] = np.abs(w[4]) + 1.0
+    x = _calibration(8, 128, seed=19, correlated=False)
+    for bits, g in ((2, 0), (4, 32), (8, 0)):
+        _check(lw, w.astype(np.float16), x, bits, g, 0.01, f"sym degenerate bits={bits} g={g}",
+               symmetric=True)
 
 
 def test_gptq_full_size_sampled(lw):

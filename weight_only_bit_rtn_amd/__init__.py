@@ -14,7 +14,8 @@ Functions mirror the C entry points:
   qgemm(x, packed, scales, zeros, K, bits, group_size) -> y      (any B)
   pack_meta(scales, zeros) -> (meta, saturated)                   compact group words
   qgemv_meta / qgemm_meta(x, packed, meta, K, bits, group_size) -> y
-  quantize_gptq(w, x_calib, bits, group_size, damp=0.01) -> dict   error-feedback codes
+  quantize_gptq(w, x_calib, bits, group_size, damp=0.01, symmetric=False) -> dict
+                                                                  error-feedback codes
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ QUANTIZE_MAX_K = 131072
 
 EXPORTED = ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
             "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta", "lowbit_gptq_workspace_bytes",
-            "lowbit_quantize_gptq", "lowbit_status_string")
+            "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym", "lowbit_status_string")
 
 _lib = None
 
@@ -65,11 +66,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowbit_gptq_workspace_bytes.restype = i64
     lib.lowbit_quantize_gptq.argtypes = [vp, i64, i64, vp, i64, ctypes.c_double, i32, i64, vp,
                                          vp, vp, vp, vp, i64, vp]
+    lib.lowbit_quantize_gptq_sym.argtypes = lib.lowbit_quantize_gptq.argtypes
     lib.lowbit_qgemv_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     for name in ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv",
                  "lowbit_qgemm", "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta",
-                 "lowbit_quantize_gptq"):
+                 "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_status_string.restype = ctypes.c_char_p
@@ -295,13 +297,22 @@ def quantize_gptq_raw(w, N, K, x, n, damp, bits, group_size, codes, packed, scal
                                                workspace_bytes, stream)
 
 
+def quantize_gptq_sym_raw(w, N, K, x, n, damp, bits, group_size, codes, packed, scales, zeros,
+                          workspace, workspace_bytes, stream) -> int:
+    return load_library().lowbit_quantize_gptq_sym(w, N, K, x, n, float(damp), bits, group_size,
+                                                   codes, packed, scales, zeros, workspace,
+                                                   workspace_bytes, stream)
+
+
 def quantize_gptq(w, x_calib, bits: int, group_size: int, damp: float = 0.01,
-                  codes: bool = True, packed: bool = True, workspace=None) -> dict:
+                  codes: bool = True, packed: bool = True, workspace=None,
+                  symmetric: bool = False) -> dict:
     """Error-feedback (GPTQ) quantization of fp16 w[N][K] with the Hessian of
     the fp16 calibration rows x_calib[n][K], on the GPU in fp64.  Returns the
     outputs of quantize_rtn plus ``status`` (device int32: 0, or 1 when the
     Hessian was not positive definite).  ``workspace``: optional uint8 device
-    tensor of at least gptq_workspace_bytes(N, K) bytes."""
+    tensor of at least gptq_workspace_bytes(N, K) bytes.  ``symmetric`` selects
+    the signed symmetric grid of quantize_rtn(symmetric=True)."""
     torch = _torch()
     _require_gpu_tensor(w, "w", torch.float16)
     _require_gpu_tensor(x_calib, "x_calib", torch.float16)
@@ -323,10 +334,11 @@ def quantize_gptq(w, x_calib, bits: int, group_size: int, damp: float = 0.01,
         out["codes"] = torch.empty((N, K), dtype=torch.uint8, device=dev)
     if packed:
         out["packed"] = torch.empty((N, packed_words(K, bits)), dtype=torch.int32, device=dev)
-    st = quantize_gptq_raw(w.data_ptr(), N, K, x_calib.data_ptr(), x_calib.shape[0], damp, bits,
-                           group_size, _ptr(out.get("codes")), _ptr(out.get("packed")),
-                           out["scales"].data_ptr(), out["zeros"].data_ptr(), ws_ptr,
-                           workspace.numel() - off, _stream_handle(dev))
-    _check(st, "lowbit_quantize_gptq")
+    raw, name = ((quantize_gptq_sym_raw, "lowbit_quantize_gptq_sym") if symmetric
+                 else (quantize_gptq_raw, "lowbit_quantize_gptq"))
+    st = raw(w.data_ptr(), N, K, x_calib.data_ptr(), x_calib.shape[0], damp, bits, group_size,
+             _ptr(out.get("codes")), _ptr(out.get("packed")), out["scales"].data_ptr(),
+             out["zeros"].data_ptr(), ws_ptr, workspace.numel() - off, _stream_handle(dev))
+    _check(st, name)
     out["status"] = workspace[off:off + 4].view(torch.int32)
     return out

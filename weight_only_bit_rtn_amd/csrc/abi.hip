@@ -220,11 +220,11 @@ int64_t lowbit_gptq_workspace_bytes(int64_t N, int64_t K) {
   return (int64_t)lowbit::gptq_workspace_bytes(N, K);
 }
 
-int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
-                         int64_t n_samples, double damp, int bits, int64_t group_size,
-                         uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
-                         int32_t* zeros, void* workspace, int64_t workspace_bytes,
-                         void* hip_stream) {
+static int gptq_checked(bool sym, const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                        int64_t n_samples, double damp, int bits, int64_t group_size,
+                        uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                        int32_t* zeros, void* workspace, int64_t workspace_bytes,
+                        void* hip_stream) {
   int rc = check_bits(bits);
   if (rc != LOWBIT_OK) return rc;
   rc = check_shape(N, K, bits, group_size);
@@ -243,8 +243,28 @@ int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_
   if (workspace_bytes < (int64_t)lowbit::gptq_workspace_bytes(N, K)) return LOWBIT_ERR_ARG;
   return hip_status(lowbit::launch_gptq(
       static_cast<const uint16_t*>(w_f16), N, K, static_cast<const uint16_t*>(x_f16), n_samples,
-      damp, bits, group_size, codes_or_null, packed_or_null, scales_f16, zeros, workspace,
+      damp, bits, group_size, sym, codes_or_null, packed_or_null, scales_f16, zeros, workspace,
       static_cast<hipStream_t>(hip_stream)));
+}
+
+int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                         int64_t n_samples, double damp, int bits, int64_t group_size,
+                         uint8_t* codes_or_null, uint32_t* packed_or_null, uint16_t* scales_f16,
+                         int32_t* zeros, void* workspace, int64_t workspace_bytes,
+                         void* hip_stream) {
+  return gptq_checked(false, w_f16, N, K, x_f16, n_samples, damp, bits, group_size,
+                      codes_or_null, packed_or_null, scales_f16, zeros, workspace,
+                      workspace_bytes, hip_stream);
+}
+
+int lowbit_quantize_gptq_sym(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                             int64_t n_samples, double damp, int bits, int64_t group_size,
+                             uint8_t* codes_or_null, uint32_t* packed_or_null,
+                             uint16_t* scales_f16, int32_t* zeros, void* workspace,
+                             int64_t workspace_bytes, void* hip_stream) {
+  return gptq_checked(true, w_f16, N, K, x_f16, n_samples, damp, bits, group_size,
+                      codes_or_null, packed_or_null, scales_f16, zeros, workspace,
+                      workspace_bytes, hip_stream);
 }
 
 const char* lowbit_status_string(int status) {

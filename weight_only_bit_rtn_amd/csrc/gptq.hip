@@ -31,8 +31,9 @@
 //     d_i to the block (a 64 x j0 x 64 product, four waves) and then the
 //     block's columns one after another (one lane per row);
 //  5. the codes are packed by the packing kernel.
-// The grid (scales, zero points) is the RTN grid of the original weights,
-// written by the RTN quantizer before step 4.
+// The grid (scales, zero points) is the RTN grid of the original weights
+// (min-max, or signed symmetric with codes from 1), written by the RTN
+// quantizer before step 4.
 #include "common.h"
 #include "kernels.h"
 
@@ -229,7 +230,8 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
 __global__ __launch_bounds__(256) void gptq_rows_kernel(
     const uint16_t* __restrict__ w, int N, int K, const double* __restrict__ L,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int G, int gsz,
-    int M, double* __restrict__ DT, uint8_t* __restrict__ codes) {
+    int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
+    uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
   __shared__ double dsm[kChunk][kRows];     // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][kRows];         // sum_{i < j} d_i R_ij of each (column, row)
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           const double wv = h_bits_to_f64(ws[lane][j]);
           const double t = wv + cb[j] / rb[j][j];
           int64_t q = (int64_t)__builtin_rint(t / s) + z;
-          q = q < 0 ? 0 : (q > M ? M : q);
+          q = q < qlo ? qlo : (q > M ? M : q);
           // (q - z) * s is exact in fp64; below 2^13 in magnitude |q - z| it
           // has at most 24 significant bits, so the fp32 step is exact and
           // the fp16 conversion is the only rounding
@@ -366,7 +368,7 @@ size_t gptq_workspace_bytes(int64_t N, int64_t K) {
 }
 
 hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
-                       int64_t n_samples, double damp, int bits, int64_t group_size,
+                       int64_t n_samples, double damp, int bits, int64_t group_size, bool sym,
                        uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
                        void* workspace, hipStream_t stream) {
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
@@ -379,7 +381,7 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   const int k = (int)K, n = (int)N;
 
   // the grid of the original weights (and placeholder codes)
-  hipError_t e = launch_quantize(w, N, K, bits, group_size, false, out_codes, nullptr, scales,
+  hipError_t e = launch_quantize(w, N, K, bits, group_size, sym, out_codes, nullptr, scales,
                                  zeros, stream);
   if (e != hipSuccess) return e;
   const int tiles = (k + 63) / 64;
@@ -400,7 +402,7 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   hipLaunchKernelGGL(gptq_rows_kernel, dim3((n + kRows - 1) / kRows), dim3(256), 0, stream, w, n,
-                     k, A, scales, zeros, G, gsz, (1 << bits) - 1, DT, out_codes);
+                     k, A, scales, zeros, G, gsz, (1 << bits) - 1, sym ? 1 : 0, DT, out_codes);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (packed) return launch_pack(out_codes, N, K, bits, packed, stream);

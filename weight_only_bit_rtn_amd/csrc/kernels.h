@@ -23,7 +23,7 @@ hipError_t launch_pack_meta(const uint16_t* scales, const int32_t* zeros, int64_
 // word, the K x K Hessian factor, the K x N residuals and N x K codes.
 size_t gptq_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
-                       int64_t n_samples, double damp, int bits, int64_t group_size,
+                       int64_t n_samples, double damp, int bits, int64_t group_size, bool sym,
                        uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
                        void* workspace, hipStream_t stream);
 
