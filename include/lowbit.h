@@ -18,8 +18,8 @@
  *  - Widths b = 2, 3, 4 and 8 (8 and 4 bits are BladeLLM's weight-only
  *    widths, "Quantization modes"; GGUF has 8-bit round-to-nearest block
  *    types beside the 4-bit ones).
- *  - The low-bit weights stay in GPU memory and are turned back into fp16 by
- *    the GPU's own cores inside the matrix product (same feature request;
+ *  - The low-bit weights stay in GPU memory and are turned back into numbers
+ *    by the GPU's own cores inside the matrix product (same feature request;
  *    "weight_only_quant" in BladeLLM model quantization, "Quantization modes",
  *    is the mode that pays off when memory bandwidth is the constraint).
  *
@@ -33,9 +33,11 @@
  *  - Packing: per row, code k occupies bits [bits*k, bits*k + bits) of a
  *    little-endian stream of 32-bit words; 3-bit codes straddle words; 8-bit
  *    code k is byte k of the row; every row starts on a word boundary.
- *  - deq(q) = fp16_rne((q - zero) * s), the product exact before one
- *    rounding;  y[b][n] = fp16_rne( sum_k x[b][k] * deq[n][k] ), accumulated
- *    in fp32 (summation order unspecified).
+ *  - deq(q) = (q - zero) * s, the exact value the code stands for (GGUF file
+ *    format, quantization-type table: weight = code x block scale + block
+ *    offset), not rounded to any format;  y[b][n] = fp16_rne( sum_k x[b][k] *
+ *    deq[n][k] ), with fp32 accumulation (summation order unspecified): within
+ *    1e-3 |y| + 1e-4 of the exact sum for inputs of the workloads' scale.
  *
  * Layouts (dense, row-major, no strides; every pointer is a DEVICE pointer
  * allocated and owned by the caller, 16-byte aligned):
@@ -128,7 +130,7 @@ LOWBIT_API int lowbit_pack(const uint8_t* codes, int64_t N, int64_t K, int bits,
 /*
  * y[B][N] = x[B][K] * deq(packed)^T for 1 <= B <= LOWBIT_QGEMV_MAX_B: the
  * fused dequantize-and-multiply of the feature request (weights kept
- * low-bit in memory, turned into fp16 by the GPU at run time).  Bandwidth-
+ * low-bit in memory, turned back into numbers by the GPU at run time).  Bandwidth-
  * bound: reads each packed word once.  B outside [0, 15] returns
  * LOWBIT_ERR_ARG.
  */
@@ -193,7 +195,7 @@ LOWBIT_API int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* p
  *    grid of the original weights, per row or per group);
  *  - columns are taken in order 0..K-1; column i's code is
  *    clamp(rint(t_i / s) + zero, 0, M) on the current fp64 weight t_i, its
- *    dequantized value deq_i = fp16_rne((q - zero) * s), and the error
+ *    dequantized value deq_i = (q - zero) * s (exact), and the error
  *    (t_i - deq_i) / Hinv_ii is fed into the later columns of the row through
  *    row i of the inverse Hessian of the columns not yet quantized;
  *  - outputs as lowbit_quantize_rtn (codes and/or packed words, scales,

@@ -178,14 +178,14 @@ class Oracle:
         sb = _bits16(scales)
         zeros = _c(zeros, np.int32)
         N, K = codes.shape
-        out = np.empty((N, K), np.uint16)
+        out = np.empty((N, K), np.float64)
         _ok(self.lib.orc_dequant(codes.ctypes.data, sb.ctypes.data, zeros.ctypes.data, N, K,
                                  bits, group_size, out.ctypes.data), "dequant")
-        return out.view(np.float16)
+        return out
 
     def matmul_f64(self, x: np.ndarray, deq: np.ndarray) -> np.ndarray:
         xb = _bits16(x)
-        db = _bits16(deq)
+        db = _c(deq, np.float64)
         B, K = xb.shape
         N = db.shape[0]
         if db.shape[1] != K:

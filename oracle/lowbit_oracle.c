@@ -23,9 +23,12 @@
  *  - Codes are packed several to a machine word ("two 4bits ... into one 8bit",
  *    "4x 2-bit weight in an uint8", "16 2-bits into an int32": [Feature
  *    Request] 4bit and 2bit and 1bit quantization support, comments).
- *  - At run time the low-bit weights are turned back into fp16 and multiplied
- *    against fp16 activations (same feature request, elephantpanda's comment
- *    on storing 4-bit weights and converting them with GPU cores).
+ *  - At run time the low-bit weights are turned back into real values and
+ *    multiplied against fp16 activations (same feature request, elephantpanda's
+ *    comment on storing 4-bit weights and converting them with GPU cores);
+ *    the weight a code stands for is code times scale, plus the offset the
+ *    zero point or block minimum carries (GGUF file format, quantization-type
+ *    table: w = q * block_scale + block_minimum).
  *
  * Readings taken where the pages leave a step open (each listed in the design
  * notes of the repository):
@@ -41,9 +44,9 @@
  *  R5 packing: per row, code k occupies bits [b*k, b*k + b) of a little-endian
  *     bitstream of 32-bit words; 3-bit codes straddle word boundaries; every
  *     row starts on a word boundary.
- *  R6 dequantized weight: deq = fp16_rne((q - zero) * s), the product taken
- *     exactly (in double it is exact: < 2^28 significant bits) and rounded
- *     once to fp16.
+ *  R6 dequantized weight: deq = (q - zero) * s, the exact real value (in
+ *     double it is exact: fewer than 44 significant bits); it is not rounded
+ *     to fp16 or to any other format.
  *  R7 reference product: y[b][n] = sum_k x[b][k] * deq[n][k] in fp64.
  */
 #include "lowbit_oracle.h"
@@ -356,7 +359,7 @@ static int spd_inverse(const double* A, int64_t K, double* inv, double* work) {
 /*  - columns are taken in their natural order i = 0 .. K-1;                */
 /*  - at column i, with Hinv the inverse Hessian of the columns not yet      */
 /*    quantized: q = clamp(rint(w_i / s) + z, 0, M) on the current fp64     */
-/*    weight, deq = fp16_rne((q - z) * s), err = (w_i - deq) / Hinv[i][i],  */
+/*    weight, deq = (q - z) * s exactly, err = (w_i - deq) / Hinv[i][i],      */
 /*    w_j -= err * Hinv[i][j] for every later column j, then column i is     */
 /*    removed from Hinv: Hinv[j][k] -= Hinv[j][i] * Hinv[i][k] / Hinv[i][i]. */
 /* Rows are independent, so any subset of rows may be passed.              */
@@ -388,7 +391,7 @@ static int gptq_codes(const uint16_t* w, int64_t N, int64_t K, const double* H, 
             if (q < minq) q = minq;
             if (q > maxq) q = maxq;
             codes[n * K + i] = (uint8_t)q;
-            const double deq = orc_f16_to_f64(orc_f64_to_f16((double)(q - z) * s));
+            const double deq = (double)(q - z) * s;
             const double err = (v - deq) / hii;
             for (int64_t j = i + 1; j < K; ++j) cur[n * K + j] -= err * hinv[i * K + j];
         }
@@ -414,10 +417,10 @@ int orc_quantize_gptq_sym(const uint16_t* w, int64_t N, int64_t K, const double*
 }
 
 /* ---------------------------------------------------------------------- */
-/* Dequantization (reading R6): deq = fp16_rne((q - zero) * scale).        */
+/* Dequantization (reading R6): deq = (q - zero) * scale, exact in fp64.    */
 /* ---------------------------------------------------------------------- */
 int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,
-                int64_t N, int64_t K, int bits, int64_t group_size, uint16_t* deq) {
+                int64_t N, int64_t K, int bits, int64_t group_size, double* deq) {
     if (!codes || !scales || !zeros || !deq || N < 0 || K <= 0 || !valid_bits(bits)) return -1;
     if (group_size < 0 || (group_size > 0 && K % group_size != 0)) return -1;
     const int64_t g = group_size == 0 ? K : group_size;
@@ -427,7 +430,7 @@ int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zer
             int64_t j = k / g;
             double s = orc_f16_to_f64(scales[n * G + j]);
             double qz = (double)((int64_t)codes[n * K + k] - (int64_t)zeros[n * G + j]);
-            deq[n * K + k] = orc_f64_to_f16(qz * s);
+            deq[n * K + k] = qz * s;
         }
     }
     return 0;
@@ -436,14 +439,14 @@ int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zer
 /* ---------------------------------------------------------------------- */
 /* Reference product (reading R7): y = x * deq^T accumulated in fp64.      */
 /* ---------------------------------------------------------------------- */
-int orc_matmul_f64(const uint16_t* x, const uint16_t* deq, int64_t B, int64_t N, int64_t K,
+int orc_matmul_f64(const uint16_t* x, const double* deq, int64_t B, int64_t N, int64_t K,
                    double* y) {
     if (!x || !deq || !y || B < 0 || N < 0 || K <= 0) return -1;
     for (int64_t b = 0; b < B; ++b) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
-                acc += orc_f16_to_f64(x[b * K + k]) * orc_f16_to_f64(deq[n * K + k]);
+                acc += orc_f16_to_f64(x[b * K + k]) * deq[n * K + k];
             y[b * N + n] = acc;
         }
     }

@@ -36,8 +36,8 @@ int orc_quantize_rtn_sym(const uint16_t* w, int64_t N, int64_t K, int bits, int6
 int orc_pack(const uint8_t* codes, int64_t N, int64_t K, int bits, uint32_t* packed);
 int orc_unpack(const uint32_t* packed, int64_t N, int64_t K, int bits, uint8_t* codes);
 int orc_dequant(const uint8_t* codes, const uint16_t* scales, const int32_t* zeros,
-                int64_t N, int64_t K, int bits, int64_t group_size, uint16_t* deq);
-int orc_matmul_f64(const uint16_t* x, const uint16_t* deq, int64_t B, int64_t N, int64_t K,
+                int64_t N, int64_t K, int bits, int64_t group_size, double* deq);
+int orc_matmul_f64(const uint16_t* x, const double* deq, int64_t B, int64_t N, int64_t K,
                    double* y);
 /* Compact metadata words (fp16 scale | int16 zero << 16); orc_pack_meta
  * returns the number of zero points saturated to the int16 range (or -1). */

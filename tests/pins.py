@@ -188,9 +188,7 @@ def check_invariants(o) -> None:
                             assert cseg[hi_i] in (M - 1, M), (label, bits, g, "max code")
                         sj = s[n, j]
                         err = np.abs(deq[n, seg] - wseg)
-                        ulp = np.spacing(np.abs(deq[n, seg]).astype(np.float16)).astype(
-                            np.float64)
-                        bound = sj * (0.5 + M * 2.0 ** -10) + ulp / 2 + np.abs(wseg) * 2.0 ** -22
+                        bound = sj * (0.5 + M * 2.0 ** -10) + np.abs(wseg) * 2.0 ** -22
                         assert np.all(err <= bound), (label, bits, g, "reconstruction error")
 
 
@@ -220,18 +218,22 @@ def check_scale_is_nearest(o) -> None:
                         assert sb[n, j] == want, (label, bits, g, hex(sb[n, j]), hex(want))
 
 
-def check_dequant_is_nearest(o) -> None:
-    """deq is the fp16 nearest to the exact rational (q - zero) * scale."""
+def check_dequant_is_exact(o) -> None:
+    """deq is exactly the rational (q - zero) * scale, with no rounding (the
+    fp16 scale taken as its exact rational value); also for zero points far
+    outside the code range."""
     rng = np.random.default_rng(5)
     for label, w in _random_weight_sets(rng):
         for bits in (2, 4, 8):
             codes, scales, zeros = o.quantize_rtn(w, bits, 32)
-            deq = o.dequant(codes, scales, zeros, bits, 32).view(np.uint16)
+            if label == "wide":
+                zeros = zeros + rng.integers(-40000, 40000, zeros.shape).astype(np.int32)
+            deq = o.dequant(codes, scales, zeros, bits, 32)
             for n in range(0, w.shape[0], 4):
                 for k in range(0, w.shape[1], 7):
                     j = k // 32
                     exact = (int(codes[n, k]) - int(zeros[n, j])) * _frac16(scales[n, j])
-                    assert deq[n, k] == _nearest_f16_bits(exact), (label, bits, n, k)
+                    assert Fraction(float(deq[n, k])) == exact, (label, bits, n, k)
 
 
 # ---------------------------------------------------------------------------
@@ -328,8 +330,7 @@ def check_sym_invariants(o) -> None:
                             assert codes[n, seg][i] == want, (label, bits, g, "extreme code")
                         sj = float(scales[n, j])
                         err = np.abs(deq[n, seg] - wseg)
-                        ulp = np.spacing(np.abs(deq[n, seg]).astype(np.float16)).astype(np.float64)
-                        bound = sj * (0.5 + qmax * 2.0 ** -10) + ulp / 2 + np.abs(wseg) * 2.0 ** -22
+                        bound = sj * (0.5 + qmax * 2.0 ** -10) + np.abs(wseg) * 2.0 ** -22
                         assert np.all(err <= bound), (label, bits, g, "reconstruction error")
 
 
@@ -499,7 +500,7 @@ def _gptq_upper_cholesky_form(w, H, scales, zeros, bits, g, qlo=0):
         z = zeros[:, i // gs].astype(np.int64)
         q = np.clip(np.rint(cur[:, i] / s).astype(np.int64) + z, qlo, M)
         codes[:, i] = q
-        deq = ((q - z) * s).astype(np.float16).astype(np.float64)
+        deq = (q - z) * s
         err = (cur[:, i] - deq) / U[i, i]
         cur[:, i + 1:] -= np.outer(err, U[i, i + 1:])
     return codes
@@ -524,7 +525,7 @@ def _gptq_reverse_cholesky_form(w, H, scales, zeros, bits, g, qlo=0):
         t = wf[:, j] + d[:, :j] @ R[:j, j] / R[j, j]
         q = np.clip(np.rint(t / s).astype(np.int64) + z, qlo, M)
         codes[:, j] = q
-        d[:, j] = wf[:, j] - ((q - z) * s).astype(np.float16).astype(np.float64)
+        d[:, j] = wf[:, j] - (q - z) * s
     return codes
 
 
@@ -582,7 +583,10 @@ def check_matmul_exact(o) -> None:
     for trial in range(20):
         B, N, K = 3, 4, 8
         x = (rng.standard_normal((B, K)) * 2).astype(np.float16)
-        d = (rng.standard_normal((N, K)) * 0.05).astype(np.float16)
+        # dequantized weights are exact products (q - z) * s: up to 19 significant
+        # bits, every one an integer multiple of 2^-24 like the fp16 values
+        d = (rng.standard_normal((N, K)) * 0.05).astype(np.float16).astype(np.float64)
+        d *= rng.integers(-255, 256, (N, K))
         if trial == 0:
             d[:] = d[0, 0]                             # all-equal weights: y = sum(x) * d
         y = o.matmul_f64(x, d)
@@ -596,7 +600,7 @@ def check_matmul_exact(o) -> None:
                 mag = sum(abs(Fraction(xi[b][k] * di[n][k], 2 ** 48)) for k in range(K))
                 assert abs(Fraction(y[b, n]) - exact) <= mag * Fraction(K, 2 ** 52), (trial, b, n)
         if trial == 0:
-            want = x.astype(np.float64).sum(axis=1, keepdims=True) * float(d[0, 0])
+            want = x.astype(np.float64).sum(axis=1, keepdims=True) * d[0, 0]
             assert np.allclose(y, np.repeat(want, N, axis=1), rtol=1e-12, atol=0)
         assert np.allclose(y, x.astype(np.float64) @ d.astype(np.float64).T, rtol=1e-12,
                            atol=1e-300)
@@ -605,7 +609,7 @@ def check_matmul_exact(o) -> None:
 ALL_CHECKS = [check_sym_worked_examples, check_sym_invariants, check_sym_scale_is_nearest,
               check_sym_bruteforce, check_f16_decode, check_f16_encode, check_worked_examples,
               check_pack_closed_forms, check_pack_bigint, check_invariants,
-              check_scale_is_nearest, check_dequant_is_nearest, check_rtn_bruteforce,
+              check_scale_is_nearest, check_dequant_is_exact, check_rtn_bruteforce,
               check_matmul_exact, check_meta_words, check_meta_round_trip,
               check_gptq_worked_example, check_gptq_hessian_closed_form,
               check_gptq_uncoupled_is_rtn, check_gptq_other_formulations,

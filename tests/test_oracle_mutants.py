@@ -37,7 +37,11 @@ MUTANTS = {
                             "double m = round(ldexp(a, 10 - e));"),
     "f16_decode_wrong_bias": ("v = ldexp((double)(1024 + f), e - 25);",
                               "v = ldexp((double)(1024 + f), e - 24);"),
-    "matmul_transposed": ("orc_f16_to_f64(deq[n * K + k])", "orc_f16_to_f64(deq[k * N + n])"),
+    "matmul_transposed": ("* deq[n * K + k];", "* deq[k * N + n];"),
+    "dequant_rounded_to_fp16": ("deq[n * K + k] = qz * s;",
+                                "deq[n * K + k] = orc_f16_to_f64(orc_f64_to_f16(qz * s));"),
+    "gptq_deq_rounded_to_fp16": ("const double deq = (double)(q - z) * s;",
+                                 "const double deq = orc_f16_to_f64(orc_f64_to_f16((double)(q - z) * s));"),
     "sym_divisor_power_of_two": ("const int qmax = (1 << (bits - 1)) - 1;",
                                  "const int qmax = (1 << (bits - 1));"),
     "sym_no_absolute_value": ("float a = fabsf((float)orc_f16_to_f64(wr[k]));",

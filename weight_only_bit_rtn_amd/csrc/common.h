@@ -23,43 +23,6 @@ __device__ __forceinline__ uint16_t f32_to_h_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-// Round an fp64 value to the nearest fp16 (ties to even) directly from its
-// bits: used where the exact value needs more than fp32's 24 bits, so a
-// detour through fp32 would round twice.
-__device__ inline uint16_t f64_to_h_bits(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
-  const int e = (int)((b >> 52) & 0x7ff);
-  uint64_t m = b & 0xFFFFFFFFFFFFFull;
-  if (e == 0x7ff) return sign | 0x7c00u | (m ? 0x200u : 0u);
-  if (e == 0) return sign;  // zero or an fp64 subnormal: far below fp16's range
-  int E = e - 1023;
-  m |= 1ull << 52;
-  // bits of the 53-bit significand that fall below the fp16 quantum
-  const int shift = (E >= -14) ? 42 : 42 + (-14 - E);
-  if (shift > 54) return sign;
-  uint64_t q = m >> shift;
-  const uint64_t rem = m & ((1ull << shift) - 1);
-  const uint64_t half = 1ull << (shift - 1);
-  if (rem > half || (rem == half && (q & 1))) ++q;
-  if (E >= -14) {
-    if (q == 2048) {
-      q = 1024;
-      ++E;
-    }
-    if (E > 15) return sign | 0x7c00u;
-    return sign | (uint16_t)(((E + 15) << 10) | (int)(q - 1024));
-  }
-  return sign | (uint16_t)q;  // q == 1024 encodes the smallest normal
-}
-
-// Full-wave sum; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 // Sum over the 64 lanes with DPP lane permutations (no LDS traffic): pairs,
 // quads, half rows, rows of 16, then the row broadcasts fold rows 0+1 into
 // row 1, 2+3 into row 3 and finally everything into row 3.  Every lane gets
@@ -78,12 +41,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 #undef LOWBIT_DPP
-
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -1,13 +1,16 @@
 // gemm.hip -- fused dequantize + small-batch matrix product on the fp16
 // matrix cores (v_mfma_f32_16x16x32_f16 of gfx950).
 //
-// y[b][n] = sum_k x[b][k] * deq(packed[n])[k] with deq = fp16_rne((q - z) * s),
-// the same contract as the matrix-vector kernel; this one is for batches
-// where the product is a real dense contraction (the matrix cores do the
-// multiply-adds, the vector ALUs only decode).  The weights are decoded from
-// their low-bit form by the GPU's own cores at run time ([Feature Request]
-// 4bit and 2bit and 1bit quantization support) and go from registers straight
-// into the MFMA B operand.
+// y[b][n] = sum_k x[b][k] * deq(packed[n])[k] with deq = (q - z) * s, the
+// exact value of each code, the same contract as the matrix-vector kernel;
+// this one is for batches where the product is a real dense contraction (the
+// matrix cores do the multiply-adds, the vector ALUs only decode).  The
+// weights are decoded from their low-bit form by the GPU's own cores at run
+// time ([Feature Request] 4bit and 2bit and 1bit quantization support) and go
+// from registers straight into the MFMA B operand: as the exact fp16
+// integers q - z, with the scale applied to the fp32 sums (one group per row,
+// and groups that hold every MFMA's codes whole), or else as (q - z) * s
+// split into an fp16 value and its exact fp16 remainder, two MFMAs.
 //
 // Work layout (one persistent workgroup of 8 waves per CU):
 //  - the weight rows are cut into groups of 16 (the MFMA's 16 columns); each
@@ -96,10 +99,11 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   constexpr int E = 2 * BT;                 // activation entries per thread and step
   constexpr int XBUF = kTileK * BP * 2 / 16;  // 16-byte entries of one activation buffer
   static_assert(XBUF == E * kThreads, "one step's activations are E entries per thread");
-  // lanes take runs of two units (else one run of all their units per step)
+  // 8-bit lanes take runs of two consecutive units (others single units)
   constexpr bool kRuns2 = BITS == 8;
-  // index of the first unit of u's run (its group constants live there)
-  auto run_start = [](int u) { return kRuns2 ? (u & ~1) : 0; };
+  // exact dequantized values in two MFMA operands (hi + lo), for group
+  // layouts whose groups do not hold every MFMA's units whole
+  constexpr bool DIRECT = GM == kPow2Groups || GM == kAnyGroups;
   // LDS: two activation tiles (later the partial sums), then per-wave scratch
   // of the exact decode path
   extern __shared__ uint4 lds[];
@@ -119,7 +123,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   const int g0 = wg * gb + min(wg, ge);
   const int g1 = g0 + gb + (wg < ge ? 1 : 0);
 
-  const uint32_t mg = magic_register();
+  uint32_t mgp[U::NPOS];
+  magic_registers<BITS>(mgp);
 
   for (int gr0 = g0; gr0 < g1; gr0 += kWaves) {
     const int RG = min(kWaves, g1 - gr0);
@@ -147,19 +152,19 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     // META: `scales` holds compact words (see RowParams), `zeros` is unused
     const RowParams<META> rp(scales, zeros, n, G);
 
-    // per-row constants (one group per row): computed once per round
-    Consts<BITS> rowc;
+    // per-row constants (one group per row): computed once per round; the
+    // row's scale multiplies the finished sum
+    PConsts<BITS> rowc;
     bool rowfast = true;
+    float row_scale = 0.0f;
     HalfParams rowp{};
     if constexpr (PERROW) {
       uint16_t s0;
       int32_t z0;
       rp.at(0, s0, z0);
       rowp = HalfParams{s0, s0, z0, z0, true, true};
-      rowfast = make_consts<BITS, false>(rowp, rowc);
-      // positions past the end of the row decode garbage words against zero
-      // activations: only a finite decode is needed there (|q - z| * s < 65504)
-      rowfast &= rowp.s_lo < 0x6C00u;
+      rowfast = make_pconsts<BITS>(rowp, rowc, false);
+      row_scale = h_bits_to_f32(s0);
     }
 
     f4_t acc[BT];
@@ -188,7 +193,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     // wide groups); 8-bit lanes, with twice the bytes per code, take runs of
     // two, so that one load instruction of the wave reads each row's eight
     // consecutive units, one 128-byte line per row, instead of four lines.
-    const int RN = kRuns2 ? (NW >= 2 ? 2 : 1) : NW;
+    const int RN = kRuns2 && NW >= 2 ? 2 : 1;
+    // index of the first unit of u's run (its group constants live there;
+    // a compile-time index after unrolling)
+    auto run_start = [](int u) { return kRuns2 ? (u & ~1) : u; };
     auto part_unit = [&](int u) { return 4 * RN * (u / RN) + RN * h + u % RN; };
     auto my_unit = [&](int t, int u) { return unit_at(t, kp * 4 * NW + part_unit(u)); };
 
@@ -304,112 +312,111 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     auto compute = [&](int t, int buf, WBuf& b) {
       if (!active) return;
       const uint4* xs = lds + buf * XBUF;
-      // Wide groups: one group for a run of units; its constants are made
-      // once per run, with every position valid.  Positions past the row end
-      // (last step of a ragged row) then decode the clamped words against
-      // zero activations: only a finite decode is needed there, which the
-      // fast path's zero-point range and s < 4096 guarantee (|q - z| * s <=
-      // 15 * s < 65504; 8-bit: z <= 255, s < 256).  The exact path keeps the
-      // per-unit validity.
-      Consts<BITS> wcc[NC];
-      bool wfast = true;
+      // One MFMA takes, for each of the 16 rows, 32 codes from 4 units (one
+      // per lane group) that lie in one span of 4 * RN consecutive units.
+      // One group per row, or groups that hold every such span whole: the
+      // codes enter as the exact integers q - z and the sum is scaled in fp32
+      // afterwards (per unit for groups).  Other group layouts: the exact
+      // dequantized value (q - z) * s enters as two fp16 operands, its fp16
+      // rounding hi and the exact remainder lo, one MFMA each.
 #pragma unroll
       for (int u = 0; u < NWMAX; ++u) {
-        if constexpr (GM == kWideGroups) {
-          if (run_start(u) == u && u < NW) {
-            wfast = true;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              HalfParams h0 = b.hp[u][c];
-              h0.v_lo = true;
-              h0.v_hi = true;
-              wfast &= make_consts<BITS, false>(h0, wcc[c]);
-              wfast &= h0.s_lo < 0x6C00u && h0.s_hi < 0x6C00u;
-            }
-          }
-        }
         if (u < NW) {
           const UnitRef ur = my_unit(t, u);
           HalfParams hp[NC];
-          Consts<BITS> cc[NC];
-          bool fast;
-          if constexpr (PERROW) {
+          PConsts<BITS> cc[NC];
+          bool fast = true;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
+          for (int c = 0; c < NC; ++c) {
+            if constexpr (PERROW) {
               hp[c] = rowp;
-              hp[c].v_lo = ur.va;
-              hp[c].v_hi = ur.vb;
               cc[c] = rowc;
+              fast = rowfast;
+            } else {
+              hp[c] = b.hp[GM == kWideGroups ? run_start(u) : u][c];
+              fast &= make_pconsts<BITS>(hp[c], cc[c], DIRECT);
             }
-            fast = rowfast;
-          } else if constexpr (GM == kWideGroups) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              hp[c] = b.hp[run_start(u)][c];  // the run's group; this unit's validity
-              hp[c].v_lo = ur.va;
-              hp[c].v_hi = ur.vb;
-              cc[c] = wcc[c];
-            }
-            fast = wfast;
-          } else {
-            fast = true;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              hp[c] = b.hp[u][c];
-              fast &= make_consts<BITS, false>(hp[c], cc[c]);
-            }
+            hp[c].v_lo = ur.va;
+            hp[c].v_hi = ur.vb;
           }
           // entries of (kp, u) for this lane: [s][bt] blocks of 64, swizzled
           const int m0 = (kp * NW + u) * Q;
           const uint4* xe = xs + (m0 * BT) * 64 + h * 16;
+          f4_t at[BT];  // wide groups: this unit's sums, scaled into acc below
+#pragma unroll
+          for (int bt = 0; bt < BT; ++bt) at[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          auto mma = [&](int s, const h2_t (&d)[4]) {
+            const h8_t bv = __builtin_bit_cast(
+                h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) {
+              const h8_t av =
+                  __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
+              if constexpr (GM == kWideGroups)
+                at[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, at[bt], 0, 0, 0);
+              else
+                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
+            }
+          };
           if (__all(fast)) {
 #pragma unroll
             for (int s = 0; s < Q; ++s) {
-              const h8_t bv = __builtin_bit_cast(
-                  h8_t, make_uint4(as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 0,
-                                                                 cc[U::cset(4 * s + 0)], mg)),
-                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 1,
-                                                                 cc[U::cset(4 * s + 1)], mg)),
-                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 2,
-                                                                 cc[U::cset(4 * s + 2)], mg)),
-                                   as_u32(fast_pair<BITS, false>(b.w[u], 4 * s + 3,
-                                                                 cc[U::cset(4 * s + 3)], mg))));
+              h2_t qz[4];
 #pragma unroll
-              for (int bt = 0; bt < BT; ++bt) {
-                const h8_t av = __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
-                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
+              for (int e = 0; e < 4; ++e) {
+                const int sl = 4 * s + e;
+                qz[e] = qz_pair<BITS>(b.w[u], sl, mgp, cc[NC == 1 ? 0 : U::cset(sl)]);
+              }
+              if constexpr (DIRECT) {
+                h2_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const h2_t s2 = cc[NC == 1 ? 0 : U::cset(4 * s + e)].s2;
+                  hi[e] = qz[e] * s2;
+                  lo[e] = __builtin_elementwise_fma(qz[e], s2, -hi[e]);
+                }
+                mma(s, hi);
+                mma(s, lo);
+              } else {
+                mma(s, qz);
               }
             }
           } else {
-            // exact per-code path (tiny or subnormal scales, zero points far
-            // from the grid, huge scales); one quad per loop trip, the unit's
+            // exact per-code path (zero points far from the codes, or, for
+            // the two-operand layouts, scales of 32 and more): the value --
+            // q - z, or (q - z) * s -- formed in fp32 and entered as its fp16
+            // rounding plus the remainder; one quad per loop trip, the unit's
             // words read back from this wave's LDS scratch
             uint32_t* wsc = slow_scratch + wave * (W * 64);
 #pragma unroll
             for (int i = 0; i < W; ++i) wsc[i * 64 + lane] = b.w[u][i];
 #pragma unroll 1
             for (int s = 0; s < Q; ++s) {
-              h2_t d[4];
+              h2_t hi[4], lo[4];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int slot = 4 * s + e;
-                const HalfParams hh = (NC == 1 || U::cset(slot) == 0) ? hp[0] : hp[NC - 1];
-                const int ql = (int)unit_code_lds<BITS>(wsc, lane, U::lo(slot));
-                const int qh = (int)unit_code_lds<BITS>(wsc, lane, U::hi(slot));
-                const uint16_t dl =
-                    hh.v_lo ? exact_deq(ql, hh.z_lo, h_bits_to_f32(hh.s_lo)) : (uint16_t)0;
-                const uint16_t dh =
-                    hh.v_hi ? exact_deq(qh, hh.z_hi, h_bits_to_f32(hh.s_hi)) : (uint16_t)0;
-                d[e] = as_h2((uint32_t)dl | ((uint32_t)dh << 16));
+                const int sl = 4 * s + e;
+                const HalfParams& hh = (NC == 1 || U::cset(sl) == 0) ? hp[0] : hp[NC - 1];
+                float vl = (float)((int)unit_code_lds<BITS>(wsc, lane, U::lo(sl)) - hh.z_lo);
+                float vh = (float)((int)unit_code_lds<BITS>(wsc, lane, U::hi(sl)) - hh.z_hi);
+                if constexpr (DIRECT) {
+                  vl *= h_bits_to_f32(hh.s_lo);
+                  vh *= h_bits_to_f32(hh.s_hi);
+                }
+                uint16_t hl, ll, hh16, lh;
+                split_f16(vl, hl, ll);
+                split_f16(vh, hh16, lh);
+                hi[e] = as_h2((uint32_t)hl | ((uint32_t)hh16 << 16));
+                lo[e] = as_h2((uint32_t)ll | ((uint32_t)lh << 16));
               }
-              const h8_t bv = __builtin_bit_cast(
-                  h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
-#pragma unroll
-              for (int bt = 0; bt < BT; ++bt) {
-                const h8_t av = __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
-                acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
-              }
+              mma(s, hi);
+              mma(s, lo);
             }
+          }
+          if constexpr (GM == kWideGroups) {
+            const float su = h_bits_to_f32(hp[0].s_lo);
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) acc[bt] += su * at[bt];
           }
         }
       }
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int b = 16 * bt + 4 * h + r;
-          red[((gl * KP + kp) * BP + b) * 16 + i16] = acc[bt][r];
+          red[((gl * KP + kp) * BP + b) * 16 + i16] = PERROW ? acc[bt][r] * row_scale : acc[bt][r];
         }
     }
     __syncthreads();
@@ -557,10 +564,10 @@ hipError_t launch_qgemm(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
-  // wide groups: a lane's run of units (at most 4 x 32 codes at 4 bits and
-  // 2 x 64 at 2 bits per step, 2 x 16 at 8 bits, starting on a multiple of
-  // that span) lies in one group
-  const bool wide = bits != 3 && gshift >= 0 && gsz >= (bits == 8 ? 32 : 128);
+  // wide groups: every MFMA's span of units (4 x 32 codes at 4 bits, 4 x 64
+  // at 2 bits, 8 x 16 at 8 bits, starting on a multiple of the span) lies in
+  // one group
+  const bool wide = bits != 3 && gshift >= 0 && gsz >= (bits == 2 ? 256 : 128);
   const int gm = G == 1 ? kPerRow : wide ? kWideGroups : gshift >= 0 ? kPow2Groups : kAnyGroups;
   const int b = (int)B, n = (int)N, k = (int)K;
   return meta ? launch_width<true>(bits, gm, b, x, packed, scales, zeros, n, k, G, gsz, gshift, y,

@@ -1,12 +1,27 @@
-// gemv_kernel.h -- fused dequantize + matrix-vector product, small batches, on the VALU.
+// gemv_kernel.h -- fused dequantize + matrix-vector product, small batches.
 //
-// y[b][n] = sum_k x[b][k] * deq(packed[n])[k], with deq the exact fp16 value
-// fp16_rne((q - z) * s) of min-max RTN.  The weights stay low-bit in HBM and
-// are converted by the GPU's own cores inside the product ([Feature Request]
-// 4bit and 2bit and 1bit quantization support: storing 4-bit weights on the
-// GPU and converting them at run time); this is the weight-only mode that
-// pays off when memory bandwidth is the constraint (BladeLLM model
-// quantization, "Quantization modes", weight_only_quant).
+// y[b][n] = sum_k x[b][k] * deq(packed[n])[k], with deq = (q - z) * s the
+// exact value a code stands for on the min-max RTN grid (the stored fp16
+// scale and integer zero: BladeLLM model quantization, "Quantization
+// algorithms", MinMax; the GGUF type table's weight = code x scale + offset).
+// The weights stay low-bit in HBM and are turned back into numbers by the
+// GPU's own cores inside the product ([Feature Request] 4bit and 2bit and
+// 1bit quantization support: storing 4-bit weights on the GPU and converting
+// them at run time); this is the weight-only mode that pays off when memory
+// bandwidth is the constraint (BladeLLM model quantization, "Quantization
+// modes", weight_only_quant).
+//
+// Arithmetic.  Per group g of a row, sum_{k in g} x_k (q_k - z) s =
+// s * sum_{k in g} x_k (q_k - z).  Each code field is OR-ed, where it sits in
+// the packed word, into the fp16 pattern of 2^(10 - p) (p its bit position)
+// and one packed subtraction of 2^(10 - p) + z leaves the exact fp16 integer
+// q - z: two VALU instructions per pair of codes (unit_decode.h).  The
+// products x * (q - z) are exact and are summed in fp32 (matrix cores at
+// batch 1 with one group per row, v_dot2_f32_f16 otherwise); the scale
+// multiplies the sum of each group (of each unit for grouped rows, of the
+// whole row otherwise).  Zero points beyond +-1024, which the subtraction
+// cannot take exactly, go through an exact per-code path that enters q - z
+// as two fp16 numbers.
 //
 // Work layout on gfx950:
 //  - one persistent workgroup of 16 waves per CU (the kernel claims the
@@ -30,13 +45,11 @@
 //    next iteration's words (two register buffers) while decoding the
 //    current one, so HBM reads stay in flight across item boundaries;
 //  - batch 1 with one group per row multiplies on the matrix cores (see
-//    below); otherwise v_dot2_f32_f16 accumulates x * deq in fp32; at the end
-//    of an item the 64 lanes are summed with DPP permutations into a partial
-//    sum in LDS, and the workgroup writes y with coalesced stores;
-//  - one group per row: the row's constants are wave-uniform (scalar
-//    registers); grouped rows take per-lane constants and per-position
-//    accumulation (see unit_decode.h), which keeps the fast decode exact for
-//    every normal scale.
+//    below); otherwise v_dot2_f32_f16 accumulates x * (q - z) in fp32; at the
+//    end of an item the 64 lanes are summed with DPP permutations into a
+//    partial sum in LDS, and the workgroup writes y with coalesced stores,
+//    applying the row's scale there (one group per row; grouped rows are
+//    scaled per unit).
 #pragma once
 
 #include "common.h"
@@ -94,81 +107,6 @@ constexpr int bytes_per_step() {
   return codes_per_step<BITS>() * BITS / 8;
 }
 
-// 2^-p of accumulator index i in per-position mode.
-template <int BITS>
-__device__ __forceinline__ float pos_scale(int i) {
-  const int p = BITS == 4 ? 4 * i : BITS == 2 ? 2 * i : i;
-  return 1.0f / (float)(1 << p);
-}
-
-// Order in which the matrix-vector kernel groups a unit's slots into quads
-// (four fp16 pairs = one 16-byte activation entry = one MFMA operand).
-// Scaled mode keeps the natural order; per-position mode puts slots of equal
-// bit position together, so that every quad feeds a single accumulator.
-template <int BITS, bool POS>
-__host__ __device__ constexpr int quad_slot(int t, int e) {
-  if constexpr (POS && BITS == 4) {
-    constexpr int tab[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
-    return tab[4 * t + e];
-  } else if constexpr (POS && BITS == 2) {
-    constexpr int tab[32] = {0, 5, 8, 13, 16, 21, 24, 29, 1, 6, 9, 14, 17, 22, 25, 30,
-                             2, 7, 10, 15, 18, 23, 26, 31, 3, 11, 19, 27, 4, 12, 20, 28};
-    return tab[4 * t + e];
-  } else {
-    return 4 * t + e;
-  }
-}
-
-// Quad and element holding slot s (inverse of quad_slot).
-template <int BITS, bool POS>
-__host__ __device__ constexpr int slot_quad_elem(int s) {
-  for (int t = 0; t < Unit<BITS>::QUADS; ++t)
-    for (int e = 0; e < 4; ++e)
-      if (quad_slot<BITS, POS>(t, e) == s) return 4 * t + e;
-  return -1;
-}
-
-template <int BITS, bool POS>
-constexpr bool quads_single_position() {
-  using U = Unit<BITS>;
-  bool seen[U::SLOTS] = {};
-  for (int t = 0; t < U::QUADS; ++t)
-    for (int e = 0; e < 4; ++e) {
-      const int s = quad_slot<BITS, POS>(t, e);
-      if (s < 0 || s >= U::SLOTS || seen[s]) return false;
-      seen[s] = true;
-      if (POS && U::pos(s) != U::pos(quad_slot<BITS, POS>(t, 0))) return false;
-    }
-  return true;
-}
-static_assert(quads_single_position<4, false>() && quads_single_position<4, true>() &&
-                  quads_single_position<2, false>() && quads_single_position<2, true>() &&
-                  quads_single_position<3, false>(),
-              "quad orders must be permutations of the slots, one bit position per quad");
-
-// Activation entry of quad t with slots in any order: eight 2-byte gathers.
-template <int BITS, bool POS>
-__device__ __forceinline__ uint4 x_entry_ordered(const uint16_t* __restrict__ xrow,
-                                                 const UnitRef& u, int t) {
-  using U = Unit<BITS>;
-  if constexpr (!POS) {
-    return x_entry<BITS>(xrow, u, t, true);
-  } else {
-    uint32_t d[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int s = quad_slot<BITS, POS>(t, e);
-      const int cl = U::lo(s), ch = U::hi(s);
-      const bool vl = BITS == 3 ? (cl < 32 ? u.va : u.vb) : u.va;
-      const bool vh = BITS == 3 ? (ch < 32 ? u.va : u.vb) : u.va;
-      const uint32_t a = vl ? xrow[unit_k<BITS>(u, cl)] : 0u;
-      const uint32_t b = vh ? xrow[unit_k<BITS>(u, ch)] : 0u;
-      d[e] = a | (b << 16);
-    }
-    return make_uint4(d[0], d[1], d[2], d[3]);
-  }
-}
-
 // The diagonal element D[j][j] of a 16x16 MFMA accumulator that lane l
 // holds: lanes whose column (l % 16) falls in their row block 4*(l / 16)
 // .. +3 hold one diagonal element each (element l % 4); the others give 0.
@@ -195,6 +133,14 @@ struct Item {
   __amdgpu_buffer_rsrc_t rs[R];
 };
 
+// Separate sums a grouped unit needs: a 3-bit unit's two periods (low /
+// high halves) may sit in different groups, and so may a 2-bit unit's two
+// 32-code periods when the group size is an odd multiple of 32.
+template <int BITS, bool PERROW, bool SPLIT>
+constexpr int unit_parts() {
+  return (BITS == 3 && !PERROW) || (BITS == 2 && SPLIT) ? 2 : 1;
+}
+
 template <int BITS, int BB, int R, bool PERROW, bool SPLIT, bool META>
 __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
@@ -203,22 +149,16 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     int RT) {
   using U = Unit<BITS>;
   constexpr int Q = U::QUADS, W = U::WORDS;
-  constexpr bool POS = !PERROW;                      // per-position accumulation
-  constexpr int NA = POS ? U::NPOS : 1;              // accumulators per (row, batch)
-  constexpr int NC = (BITS == 2 && SPLIT) ? 2 : 1;   // constant sets per unit
-  // scale/zero loads per row and unit: a 3-bit unit's two periods (lo / hi
-  // halves) may sit in different groups, and so may a 2-bit unit's two periods
-  constexpr int NL = (BITS == 3 && !PERROW) || (BITS == 2 && SPLIT) ? 2 : 1;
+  constexpr int NL = unit_parts<BITS, PERROW, SPLIT>();
+  constexpr bool HALVES = BITS == 3 && !PERROW;  // the two halves belong to different groups
   // Batch 1, one group per row: the multiply-accumulate runs on the matrix
-  // cores (grouped layouts keep v_dot2: their per-position accumulators would
-  // need one MFMA accumulator tile per bit position, which costs more
-  // registers than it saves).  Each lane
-  // puts its own 8 activations (A operand) and its own 8 dequantized weights
-  // (B operand) into v_mfma_f32_16x16x32_f16; the diagonal D[j][j] of the
-  // result is then the dot product over lanes j, j+16, j+32, j+48, and the
-  // VALU only decodes.  (Off-diagonal entries mix lanes and are ignored.)
+  // cores.  Each lane puts its own 8 activations (A operand) and its own 8
+  // values q - z (B operand) into v_mfma_f32_16x16x32_f16; the diagonal
+  // D[j][j] of the result is then the dot product over lanes j, j+16, j+32,
+  // j+48, and the VALU only decodes.  (Off-diagonal entries mix lanes and
+  // are ignored.)
   constexpr bool MD = BB == 1 && PERROW;
-  // LDS: activations [J][Q][BB][64] | per-wave slow-path scratch |
+  // LDS: activations [J][Q][BB][64] | per-wave scratch of the exact path |
   //      partial sums [RT * R rows][BB][JC] | work counter
   extern __shared__ uint4 xs[];
 
@@ -254,11 +194,6 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     int32_t z[R][NL];
   };
 
-  // META: `scales` holds the compact words (4 bytes per group) and the
-  // zeros descriptor is empty
-  const auto srs =
-      rsrc(scales, (uint32_t)min((int64_t)N * G * (META ? 4 : 2), (int64_t)0x7fffffff));
-  const auto zrs = rsrc(zeros, META ? 0u : (uint32_t)min((int64_t)N * G * 4, (int64_t)0x7fffffff));
   int rt0 = t0;  // first tile of the current round
   int nit = 0;   // items of the current round
 
@@ -295,34 +230,25 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const int j = t.j;
     const uint32_t step = (uint32_t)j * bytes_per_step<BITS>();
     const uint32_t va_off = off_a + step, vb_off = off_b + step;
-    UnitRef u;
-    if constexpr (!PERROW) u = gemv_unit<BITS>(j, lane, K);
-    // scale / zero loads first: a wait for this step's words then also
-    // covers them, whatever the number of loads issued after
+    // zero points (and for grouped rows the scales) before the words, so the
+    // wait for the words also covers them
+    if constexpr (PERROW) {
+      if (j == t.jb) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = min(n0 + r, N - 1);
-      if constexpr (PERROW) {
-        if (j == t.jb) {
-          // vector (buffer) loads on purpose: a scalar load would share the
-          // lgkm counter with the LDS activation reads, and every wait on
-          // those would then also wait for this prefetch to come from HBM
-          const uint32_t nn = (uint32_t)n + 0u * (uint32_t)lane;
-          if constexpr (META) {
-            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(srs, 4u * nn, 0, 0);
-            b.s[r][0] = (uint16_t)v;
-            b.z[r][0] = (int32_t)v >> 16;
-          } else {
-            b.s[r][0] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(srs, 2u * nn, 0, 0);
-            b.z[r][0] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(zrs, 4u * nn, 0, 0);
-          }
+        for (int r = 0; r < R; ++r) {
+          uint16_t sb;
+          RowParams<META>(scales, zeros, min(n0 + r, N - 1), G).at(0, sb, b.z[r][0]);
         }
-      } else {
-        const RowParams<META> rp(scales, zeros, n, G);
+      }
+    } else {
+      const UnitRef u = gemv_unit<BITS>(j, lane, K);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const RowParams<META> rp(scales, zeros, min(n0 + r, N - 1), G);
 #pragma unroll
         for (int c = 0; c < NL; ++c) {
           const int kk = BITS == 3 ? (c == 0 ? u.ka : u.kb) : u.ka + 32 * c;
-          const bool v = BITS == 3 ? (c == 0 ? u.va : u.vb) : u.va;
+          const bool v = BITS == 3 ? (c == 0 ? u.va : u.vb) : kk < K;
           const int g = v ? group_of(kk, gsz, gshift) : 0;
           rp.at(g, b.s[r][c], b.z[r][c]);
         }
@@ -350,71 +276,89 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     }
   };
 
-  float acc[R][BB][NA];
+  float acc[R][BB];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int b = 0; b < BB; ++b)
+    for (int b = 0; b < BB; ++b) acc[r][b] = 0.0f;
+  f4_t dacc[R];
 #pragma unroll
-      for (int a = 0; a < NA; ++a) acc[r][b][a] = 0.0f;
-  f4_t dacc[R][MD ? NA : 1];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int a = 0; a < (MD ? NA : 1); ++a) dacc[r][a] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < R; ++r) dacc[r] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const uint32_t mg = magic_register();
-  Consts<BITS> rowc[R];
-  uint16_t rows_s[R];
-  int32_t rows_z[R];
+  uint32_t mgp[U::NPOS];
+  magic_registers<BITS>(mgp);
+  PConsts<BITS> rowc[R];  // one group per row: the rows' constants (wave-uniform)
+  int32_t row_z[R];
   bool rowfast = true;
 
   auto compute = [&](const Item<R>& t, Buf& b) {
     const int j = t.j;
     const UnitRef u = gemv_unit<BITS>(j, lane, K);
-    HalfParams hp[R][NC];
-    Consts<BITS> cc[R][NC];
+    PConsts<BITS> cc[R][NL];
+    HalfParams hp[R][NL];
     bool fast = true;
     if constexpr (PERROW) {
       if (j == t.jb) {
         rowfast = true;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          rows_s[r] = (uint16_t)uniform(b.s[r][0]);
-          rows_z[r] = (int32_t)uniform((uint32_t)b.z[r][0]);
-          HalfParams h{rows_s[r], rows_s[r], rows_z[r], rows_z[r], true, true};
-          rowfast &= make_consts<BITS, false>(h, rowc[r]);
-          // Positions past the end of the row (last K step of a ragged row)
-          // are decoded from zero words without masking: their activations
-          // are staged as zeros, so only a finite decode is needed there,
-          // which |q - z| * s <= 15 * s < 65504 guarantees (8-bit codes:
-          // the fast-path bounds z <= 255, s < 256).
-          rowfast &= rows_s[r] < 0x6C00u;  // s < 4096
+          row_z[r] = (int32_t)uniform((uint32_t)b.z[r][0]);
+          const HalfParams h{0, 0, row_z[r], row_z[r], true, true};
+          rowfast &= make_pconsts<BITS>(h, rowc[r], false);
 #pragma unroll
-          for (int i = 0; i < U::NPOS; ++i) {
-            rowc[r].hz[i] = as_h2(uniform(as_u32(rowc[r].hz[i])));
-            rowc[r].hs[i] = as_h2(uniform(as_u32(rowc[r].hs[i])));
-          }
+          for (int i = 0; i < U::NPOS; ++i) rowc[r].hz[i] = as_h2(uniform(as_u32(rowc[r].hz[i])));
         }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) cc[r][0] = rowc[r];
+      for (int r = 0; r < R; ++r) {
+        cc[r][0] = rowc[r];
+        hp[r][0] = HalfParams{0, 0, row_z[r], row_z[r], u.va, u.vb};
+      }
       fast = rowfast;
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          if constexpr (BITS == 3)  // lo half from period a, hi half from period b
+        for (int c = 0; c < NL; ++c) {
+          if constexpr (HALVES)  // lo half from period a, hi half from period b
             hp[r][c] = HalfParams{b.s[r][0], b.s[r][1], b.z[r][0], b.z[r][1], u.va, u.vb};
           else
             hp[r][c] = HalfParams{b.s[r][c], b.s[r][c], b.z[r][c], b.z[r][c], u.va, u.vb};
-          fast &= make_consts<BITS, true>(hp[r][c], cc[r][c]);
+          fast &= make_pconsts<BITS>(hp[r][c], cc[r][c], false);
         }
       fast = __all(fast);
     }
+    // the part of slot s (grouped rows: which group sum it belongs to)
+    auto part_of = [](int s) { return (BITS == 2 && SPLIT) ? U::cset(s) : 0; };
 
     const uint4* xj = xs + (int64_t)j * Q * BB * 64 + lane;
+    // grouped rows: the unit's sums per part, scaled into acc at the end
+    float ts[R][BB][NL];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+        for (int c = 0; c < NL; ++c) ts[r][bb][c] = 0.0f;
+    // x * d of one slot into the accumulators of row r
+    auto accumulate = [&](int r, int s, h2_t d, const uint4 (&xq)[BB], int e) {
+#pragma unroll
+      for (int bb = 0; bb < BB; ++bb) {
+        const uint32_t xv = e == 0 ? xq[bb].x : e == 1 ? xq[bb].y : e == 2 ? xq[bb].z : xq[bb].w;
+        const h2_t xh = as_h2(xv);
+        if constexpr (PERROW) {
+          acc[r][bb] = __builtin_amdgcn_fdot2(d, xh, acc[r][bb], false);
+        } else if constexpr (HALVES) {
+          ts[r][bb][0] = __builtin_fmaf((float)d.x, (float)xh.x, ts[r][bb][0]);
+          ts[r][bb][NL - 1] = __builtin_fmaf((float)d.y, (float)xh.y, ts[r][bb][NL - 1]);
+        } else if (NL == 1 || part_of(s) == 0) {  // (no run-time index into registers)
+          ts[r][bb][0] = __builtin_amdgcn_fdot2(d, xh, ts[r][bb][0], false);
+        } else {
+          ts[r][bb][NL - 1] = __builtin_amdgcn_fdot2(d, xh, ts[r][bb][NL - 1], false);
+        }
+      }
+    };
+
     if (MD && fast) {
       // all activation quads of the step first: one LDS wait per step
       uint4 xq[Q];
@@ -425,21 +369,15 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         const h8_t av = __builtin_bit_cast(h8_t, xq[q]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          h2_t d[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = quad_slot<BITS, POS>(q, e);
-            const int c = NC == 1 ? 0 : U::cset(s);
-            d[e] = fast_pair<BITS, POS>(b.w[r], s, cc[r][c], mg);
-          }
           const h8_t bv = __builtin_bit_cast(
-              h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
-          const int a = POS ? U::pidx(U::pos(quad_slot<BITS, POS>(q, 0))) : 0;
-          dacc[r][MD ? a : 0] =
-              __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, dacc[r][MD ? a : 0], 0, 0, 0);
+              h8_t, make_uint4(as_u32(qz_pair<BITS>(b.w[r], 4 * q + 0, mgp, cc[r][0])),
+                               as_u32(qz_pair<BITS>(b.w[r], 4 * q + 1, mgp, cc[r][0])),
+                               as_u32(qz_pair<BITS>(b.w[r], 4 * q + 2, mgp, cc[r][0])),
+                               as_u32(qz_pair<BITS>(b.w[r], 4 * q + 3, mgp, cc[r][0]))));
+          dacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, dacc[r], 0, 0, 0);
         }
       }
-    } else if (!MD && fast) {
+    } else if (fast) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         uint4 xq[BB];
@@ -450,46 +388,51 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int s = 4 * q + e;
-            const int c = NC == 1 ? 0 : U::cset(s);
-            const h2_t d = fast_pair<BITS, POS>(b.w[r], s, cc[r][c], mg);
-            const int a = POS ? U::pidx(U::pos(s)) : 0;
-#pragma unroll
-            for (int bb = 0; bb < BB; ++bb) {
-              const uint32_t xv = e == 0 ? xq[bb].x : e == 1 ? xq[bb].y : e == 2 ? xq[bb].z : xq[bb].w;
-              acc[r][bb][a] = __builtin_amdgcn_fdot2(d, as_h2(xv), acc[r][bb][a], false);
-            }
+            accumulate(r, s, qz_pair<BITS>(b.w[r], s, mgp, cc[r][NL == 1 ? 0 : part_of(s)]), xq, e);
           }
       }
     } else {
-      // Exact per-code path (rare: tiny or subnormal scales, zero points far
-      // from the grid).  Kept compact: one slot per loop trip, the unit's
-      // words read back from this wave's LDS scratch.
+      // Exact per-code path (zero points beyond +-1024): q - z formed in
+      // fp32 and entered as two fp16 numbers (its rounding and the
+      // remainder).  Kept compact: one slot per loop trip, the unit's words
+      // read back from this wave's LDS scratch.
       uint32_t* wsc = slow_scratch + wave * (W * 64);
-      const uint32_t* xj32 = reinterpret_cast<const uint32_t*>(xs + (int64_t)j * Q * BB * 64);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int i = 0; i < W; ++i) wsc[i * 64 + lane] = b.w[r][i];
 #pragma unroll 1
         for (int s = 0; s < U::SLOTS; ++s) {
-          const int c = NC == 1 ? 0 : U::cset(s);
-          const HalfParams h =
-              PERROW ? HalfParams{rows_s[r], rows_s[r], rows_z[r], rows_z[r], u.va, u.vb}
-                     : c == 0 ? hp[r][0] : hp[r][NC - 1];
-          const int ql = (int)unit_code_lds<BITS>(wsc, lane, U::lo(s));
-          const int qh = (int)unit_code_lds<BITS>(wsc, lane, U::hi(s));
-          const uint16_t dl = h.v_lo ? exact_deq(ql, h.z_lo, h_bits_to_f32(h.s_lo)) : (uint16_t)0;
-          const uint16_t dh = h.v_hi ? exact_deq(qh, h.z_hi, h_bits_to_f32(h.s_hi)) : (uint16_t)0;
-          const h2_t d = as_h2((uint32_t)dl | ((uint32_t)dh << 16));
-          const int qe = MD ? slot_quad_elem<BITS, POS>(s) : s;
-          const int q = qe >> 2, e = qe & 3;
+          const HalfParams& h = (HALVES || part_of(s) == 0) ? hp[r][0] : hp[r][NL - 1];
+          const float vl = (float)((int)unit_code_lds<BITS>(wsc, lane, U::lo(s)) - h.z_lo);
+          const float vh = (float)((int)unit_code_lds<BITS>(wsc, lane, U::hi(s)) - h.z_hi);
+          uint16_t hl, ll, hh, lh;
+          split_f16(vl, hl, ll);
+          split_f16(vh, hh, lh);
+          const int q = s >> 2, e = s & 3;
+          uint4 xq[BB];
 #pragma unroll
-          for (int bb = 0; bb < BB; ++bb) {
-            const uint32_t xv = xj32[((q * BB + bb) * 64 + lane) * 4 + e];
-            acc[r][bb][0] = __builtin_amdgcn_fdot2(d, as_h2(xv), acc[r][bb][0], false);
-          }
+          for (int bb = 0; bb < BB; ++bb) xq[bb] = xj[(q * BB + bb) * 64];
+          accumulate(r, s, as_h2((uint32_t)hl | ((uint32_t)hh << 16)), xq, e);
+          accumulate(r, s, as_h2((uint32_t)ll | ((uint32_t)lh << 16)), xq, e);
         }
       }
+    }
+    if constexpr (!PERROW) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          const float sl = h_bits_to_f32(hp[r][c].s_lo);
+          const float sh = h_bits_to_f32(hp[r][c].s_hi);
+#pragma unroll
+          for (int bb = 0; bb < BB; ++bb) {
+            if constexpr (HALVES)
+              acc[r][bb] += c == 0 ? sl * ts[r][bb][0] : sh * ts[r][bb][NL - 1];
+            else
+              acc[r][bb] += sl * ts[r][bb][c];
+          }
+        }
     }
 
     if (j == t.je - 1) {
@@ -498,20 +441,14 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
       for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int bb = 0; bb < BB; ++bb) {
-          float v = acc[r][bb][0];
-#pragma unroll
-          for (int a = 1; a < NA; ++a) v += acc[r][bb][a] * pos_scale<BITS>(a);
+          float v = acc[r][bb];
+          acc[r][bb] = 0.0f;
           if constexpr (MD) {
-#pragma unroll
-            for (int a = 0; a < NA; ++a) {
-              v += mfma_diag(dacc[r][a], lane) * pos_scale<BITS>(a);
-              dacc[r][a] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+            v += mfma_diag(dacc[r], lane);
+            dacc[r] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
           }
           v = wave_sum_dpp(v);
           if (lane == 0) part[((t.tl * R + r) * BB + bb) * JC + t.c] = v;
-#pragma unroll
-          for (int a = 0; a < NA; ++a) acc[r][bb][a] = 0.0f;
         }
       }
     }
@@ -536,8 +473,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         const int q = rest % Q;
         const int jj = rest / Q;
         const UnitRef uu = gemv_unit<BITS>(jj, l, K);
-        xs[e] = MD ? x_entry_ordered<BITS, POS>(x + (int64_t)b * K, uu, q)
-                   : x_entry<BITS>(x + (int64_t)b * K, uu, q, true);
+        xs[e] = x_entry<BITS>(x + (int64_t)b * K, uu, q, true);
       }
     }
     __syncthreads();
@@ -560,7 +496,8 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     }
     __syncthreads();
 
-    // the round's outputs: sum the K chunks in order, coalesced stores
+    // the round's outputs: sum the K chunks in order (one group per row: times
+    // the row's scale), coalesced stores
     const int row0 = rt0 * R;
     const int nrows = min((rt0 + ntl) * R, N) - row0;
     for (int e = tid; e < nrows * BB; e += kThreads) {
@@ -568,6 +505,12 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
       const float* pp = part + (rr * BB + bb) * JC;
       float v = 0.0f;
       for (int c = 0; c < JC; ++c) v += pp[c];
+      if constexpr (PERROW) {
+        uint16_t sb;
+        int32_t zz;
+        RowParams<META>(scales, zeros, row0 + rr, G).at(0, sb, zz);
+        v *= h_bits_to_f32(sb);
+      }
       y[(int64_t)bb * N + row0 + rr] = f32_to_h_bits(v);
     }
     __syncthreads();  // partial sums and counter are reused by the next round
@@ -580,8 +523,7 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
                     hipStream_t stream) {
   using U = Unit<BITS>;
   // two rows per wave where the accumulators leave room for a second row
-  constexpr int NA = PERROW ? 1 : U::NPOS;
-  constexpr int R = (BB <= 4 && BB * NA <= 16) ? 2 : 1;
+  constexpr int R = BB <= 4 ? 2 : 1;
   const int J = (K + codes_per_step<BITS>() - 1) / codes_per_step<BITS>();
   const int T = (N + R - 1) / R;
   const int cus = device_cu_count();

@@ -31,7 +31,8 @@
 //     d_i to the block (a 64 x j0 x 64 product, four waves) and then the
 //     block's columns one after another (one lane per row);
 //  5. the codes are packed by the packing kernel.
-// The grid (scales, zero points) is the RTN grid of the original weights
+// deq_i = (q_i - z) * s is the exact value code q_i stands for.  The grid
+// (scales, zero points) is the RTN grid of the original weights
 // (min-max, or signed symmetric with codes from 1), written by the RTN
 // quantizer before step 4.
 #include "common.h"
@@ -334,14 +335,8 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           const double t = wv + cb[j] / rb[j][j];
           int64_t q = (int64_t)__builtin_rint(t / s) + z;
           q = q < qlo ? qlo : (q > M ? M : q);
-          // (q - z) * s is exact in fp64; below 2^13 in magnitude |q - z| it
-          // has at most 24 significant bits, so the fp32 step is exact and
-          // the fp16 conversion is the only rounding
-          const int64_t qz = q - z;
-          const double prod = (double)qz * s;
-          const double deq = (qz > -8192 && qz < 8192)
-                                 ? (double)(_Float16)(float)prod
-                                 : h_bits_to_f64(f64_to_h_bits(prod));
+          // the dequantized weight (q - z) * s, exact in fp64
+          const double deq = (double)(q - z) * s;
           const double d = wv - deq;
           reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
           if (valid) DT[(int64_t)col * N + row] = d;

@@ -1,10 +1,11 @@
-// unit_decode.h -- turning packed b-bit codes into exact fp16 dequantized pairs.
+// unit_decode.h -- where the packed b-bit codes sit, and how they enter
+// fp16 arithmetic.
 //
-// The product y = x * deq(W)^T needs, per weight, deq = fp16_rne((q - z) * s)
-// computed exactly (the stored-fp16 scale and integer zero of min-max RTN:
-// BladeLLM model quantization, "Quantization algorithms", MinMax; OPTQ
-// reproducibility card, "Experiment Setup" row).  The decode works on
-// "units": the packed bits one lane loads at once.
+// The products need, per weight, the value deq = (q - z) * s a code stands
+// for (the stored fp16 scale and integer zero of min-max RTN: BladeLLM model
+// quantization, "Quantization algorithms", MinMax; OPTQ reproducibility card,
+// "Experiment Setup" row).  The decode works on "units": the packed bits one
+// lane loads at once.
 //
 //   4-bit: one 32-code period, 4 words (one 16-byte load)
 //   2-bit: two consecutive periods, 64 codes, 4 words (one 16-byte load)
@@ -12,28 +13,22 @@
 //          3 words each (two 12-byte loads)
 //   8-bit: 16 codes, 4 words (one 16-byte load)
 //
-// A unit yields 16 or 32 "slots": pairs of codes (lo, hi) that end up in the
-// low and high fp16 halves of one 32-bit register, so that the fp16 math runs
-// two codes per instruction.  A slot's code field sits at bit position p of
-// both halves; OR-ing it into the fp16 pattern of 1024 (0x6400) gives the
-// exact fp16 value 1024 + q*2^p ("magic number" conversion), then
-//
-//   deq = ((1024 + q*2^p) - (1024 + z*2^p)) * (s*2^-p)
-//
-// where the subtraction is exact (both operands are integers below 2048) and
-// the product (q - z) * 2^p * s * 2^-p = (q - z) * s is rounded once, by the
-// fp16 multiply.  This is exact whenever 1024 + z*2^p is an integer in
-// [0, 2047] and s*2^-p is an fp16 number; the per-group check below tests
-// both, and groups that fail it take a slower per-code path that computes
-// the exact product in fp64 and rounds it to fp16 directly.
+// A unit yields 8, 16 or 32 "slots": pairs of codes (lo, hi) that end up in
+// the low and high fp16 halves of one 32-bit register, so that the fp16 math
+// runs two codes per instruction.  A slot's code field sits at bit position p
+// of both halves (3-bit: windows of ten codes are first cut out of the
+// straddling words with funnel shifts and byte permutes).  Masked out alone,
+// under a zero exponent field, the field is the exact fp16 subnormal
+// q * 2^(p - 24) (the matrix-vector kernel's decode); OR-ed into the fp16
+// pattern of 2^(10 - p) it is the exact fp16 integer 2^(10 - p) + q, from
+// which one subtraction gives q - z exactly (the matrix-core kernel's).
 //
 // The activations are stored on chip in the same slot order, so no
 // per-weight shuffle is needed in the inner loop.
 //
-// 8-bit codes cannot use a shifted field (1024 + q*2^p stays below 2048 only
-// for p = 0), so each slot pairs two neighbouring bytes of one word and a
-// single byte permute drops them under the two 0x64 exponent bytes of the
-// magic register: p = 0 for every slot.
+// 8-bit codes have no room for a shift (p = 0 for every slot): each slot
+// pairs two neighbouring bytes of one word, which one byte permute places in
+// the two halves, under zero bytes or under the 0x64 exponent bytes of 1024.
 #pragma once
 
 #include "common.h"
@@ -158,8 +153,8 @@ struct Unit<8> {
   __host__ __device__ static constexpr bool uses(int p) { return p == 0; }
   static constexpr int NPOS = 1;
   __host__ __device__ static constexpr int pidx(int) { return 0; }
-  // v_perm_b32 selectors 0..3 pick bytes of the word, 4..7 bytes of the magic
-  // register 0x64006400 (5 and 7 are its 0x64 bytes)
+  // v_perm_b32 selectors 0..3 pick bytes of the word, 4..7 bytes of mg, whose
+  // bytes 1 and 3 become the halves' high bytes (0x64: 1024 + q; 0: q * 2^-24)
   __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
                                                     uint32_t mg) {
     return __builtin_amdgcn_perm(mg, w[s >> 1], (s & 1) ? 0x07030502u : 0x07010500u);
@@ -221,82 +216,6 @@ struct HalfParams {
   bool v_lo, v_hi;
 };
 
-// Decode constants of one unit, indexed by bit position (pidx).
-//  hz[i] = 1024 + z * 2^p                          (both modes)
-//  hs[i] = s * 2^-p   (scaled mode: one accumulator per output)
-//  hs[0] = s          (per-position mode: the product comes out scaled by 2^p
-//                      and is accumulated separately per p, rescaled at the end)
-template <int BITS>
-struct Consts {
-  h2_t hz[Unit<BITS>::NPOS];
-  h2_t hs[Unit<BITS>::NPOS];
-};
-
-// Constants from integer operations on the bit patterns (so uniform inputs
-// stay in scalar registers):
-//  - 1024 + z*2^p for 0 <= z*2^p < 1024 is the fp16 pattern 0x6400 | (z << p);
-//  - s*2^-p is s with its exponent field lowered by p, exact as long as the
-//    result stays a normal number (exponent field of s above p).
-// Fast decode conditions per half (both modes): 0 <= z <= 1023 >> PMAX;
-//  scaled mode: exponent field of s >= PMAX + 1;
-//  per-position mode: s normal and s < 8, so that (q - z) * s * 2^p stays in
-//  fp16's normal range, where scaling by 2^p commutes with the rounding.
-// 8-bit codes (no shifted positions): 0 <= z <= 255 and s < 256, so that
-//  |q - z| * s < 65504 for every code (also for decoded words past the end of
-//  a row), subnormal scales included (the single fp16 multiply rounds them
-//  correctly).
-template <int BITS, bool POS>
-__device__ __forceinline__ bool half_fast(uint32_t sb, int32_t z) {
-  constexpr int PMAX = Unit<BITS>::PMAX;
-  if constexpr (BITS == 8) return (uint32_t)z <= 255u && sb < 0x5C00u;
-  const bool zok = (uint32_t)z <= (1023u >> PMAX);
-  const bool sok = POS ? (sb >= 0x0400u && sb < 0x4800u) : (sb >= (uint32_t)(PMAX + 1) << 10);
-  return zok && sok;
-}
-
-template <int BITS, bool POS>
-__device__ __forceinline__ bool make_consts(const HalfParams& hp, Consts<BITS>& c) {
-  using U = Unit<BITS>;
-  const uint32_t s2 = (uint32_t)hp.s_lo | ((uint32_t)hp.s_hi << 16);
-  const uint32_t z2 = ((uint32_t)hp.z_lo & 0xffffu) | ((uint32_t)hp.z_hi << 16);
-  const uint32_t keep = (hp.v_lo ? 0x0000ffffu : 0u) | (hp.v_hi ? 0xffff0000u : 0u);
-#pragma unroll
-  for (int p = 0; p <= U::PMAX; ++p) {
-    if (!U::uses(p)) continue;
-    const int i = U::pidx(p);
-    c.hz[i] = as_h2(0x64006400u + (z2 << p));
-    if (!POS) c.hs[i] = as_h2((s2 - ((uint32_t)p << 10) * 0x10001u) & keep);
-  }
-  if (POS) c.hs[0] = as_h2(s2 & keep);
-  const bool fl = !hp.v_lo || half_fast<BITS, POS>(hp.s_lo, hp.z_lo);
-  const bool fh = !hp.v_hi || half_fast<BITS, POS>(hp.s_hi, hp.z_hi);
-  return fl && fh;
-}
-
-// fp16_rne((q - z) * s) for any code, zero point and scale: the product is
-// formed in fp32 and rounded to odd (its last bit records inexactness), which
-// makes the following fp32 -> fp16 rounding the correctly rounded result
-// (fp32 carries at least two more bits than fp16).
-__device__ __forceinline__ uint16_t exact_deq(int q, int z, float s) {
-  const float qz = (float)(q - z);  // exact: |q - z| < 2^24
-  const float p = qz * s;
-  const float e = __builtin_fmaf(qz, s, -p);  // exact remainder of the product
-  uint32_t pb = __builtin_bit_cast(uint32_t, p);
-  if (e != 0.0f && (pb & 1u) == 0u) pb += ((e > 0.0f) == (p > 0.0f)) ? 1u : 0xffffffffu;
-  return f32_to_h_bits(__builtin_bit_cast(float, pb));
-}
-
-template <int BITS>
-__device__ __forceinline__ h2_t slow_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
-                                          const HalfParams& hp) {
-  using U = Unit<BITS>;
-  const int ql = (int)U::code(w, U::lo(s));
-  const int qh = (int)U::code(w, U::hi(s));
-  const uint16_t dl = hp.v_lo ? exact_deq(ql, hp.z_lo, h_bits_to_f32(hp.s_lo)) : (uint16_t)0;
-  const uint16_t dh = hp.v_hi ? exact_deq(qh, hp.z_hi, h_bits_to_f32(hp.s_hi)) : (uint16_t)0;
-  return as_h2((uint32_t)dl | ((uint32_t)dh << 16));
-}
-
 // Code c of a unit whose words are stored column-wise in LDS (word i of lane
 // l at w[i * 64 + l]); c may be a run-time value.
 template <int BITS>
@@ -312,26 +231,69 @@ __device__ __forceinline__ uint32_t unit_code_lds(const uint32_t* w, int lane, i
   return v & ((1u << BITS) - 1u);
 }
 
-// The fp16 bit pattern of 1024.0 in both halves, held in a vector register
-// (the kernels hide its value from the compiler once, so every field
-// extraction becomes a single v_and_or_b32 with the mask in a scalar register;
-// gfx9 VOP3 encodings cannot carry two literals).
-constexpr uint32_t kMagic1024 = 0x64006400u;
-
-__device__ __forceinline__ uint32_t magic_register() {
-  uint32_t mg = kMagic1024;
-  asm volatile("" : "+v"(mg));
-  return mg;
+// fp16 pattern of 2^(10 - p) in both halves for every field position p,
+// held in vector registers (gfx9 VOP3 encodings carry no literal, and the
+// field mask takes the one scalar operand, so each field extraction is one
+// v_and_or_b32): OR-ed onto a field q * 2^p it gives the exact 2^(10 - p) + q.
+template <int BITS>
+__device__ __forceinline__ void magic_registers(uint32_t (&mgp)[Unit<BITS>::NPOS]) {
+  using U = Unit<BITS>;
+#pragma unroll
+  for (int p = 0; p <= U::PMAX; ++p) {
+    if (!U::uses(p)) continue;
+    uint32_t v = (uint32_t)(25 - p) * 0x04000400u;
+    asm volatile("" : "+v"(v));
+    mgp[U::pidx(p)] = v;
+  }
 }
 
-// Fast pair of slot s; in per-position mode the result is 2^p * deq.
-template <int BITS, bool POS>
-__device__ __forceinline__ h2_t fast_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
-                                          const Consts<BITS>& c, uint32_t mg) {
+// Decode constants of one unit: for every field position p, the fp16 value
+// 2^(10 - p) + z of each half, so that (2^(10 - p) + q) - (2^(10 - p) + z) =
+// q - z exactly; and the halves' scales.
+template <int BITS>
+struct PConsts {
+  h2_t hz[Unit<BITS>::NPOS];
+  h2_t s2;
+};
+
+// The fast decode needs 2^(10 - p) + z and q - z to be fp16 integers (|z| <=
+// 1024 suffices); the two-operand form (direct) also keeps (q - z) * s finite
+// (0 <= s < 32, an fp16 pattern below 0x5000).  A half's two bytes of 3-bit
+// units may come from different groups; other widths share one zero.
+template <int BITS>
+__device__ __forceinline__ bool make_pconsts(const HalfParams& hp, PConsts<BITS>& c,
+                                             bool direct) {
+  using U = Unit<BITS>;
+#pragma unroll
+  for (int p = 0; p <= U::PMAX; ++p) {
+    if (!U::uses(p)) continue;
+    const float base = (float)(1 << (10 - p));
+    const uint32_t lo = f32_to_h_bits(base + (float)hp.z_lo);
+    const uint32_t hi = BITS == 3 ? f32_to_h_bits(base + (float)hp.z_hi) : lo;
+    c.hz[U::pidx(p)] = as_h2(lo | (hi << 16));
+  }
+  c.s2 = as_h2((uint32_t)hp.s_lo | ((uint32_t)hp.s_hi << 16));
+  bool ok = hp.z_lo >= -1024 && hp.z_lo <= 1024 && hp.z_hi >= -1024 && hp.z_hi <= 1024;
+  if (direct) ok = ok && hp.s_lo < 0x5000u && hp.s_hi < 0x5000u;
+  return ok;
+}
+
+// q - z of both codes of slot s, exact: (2^(10 - p) + q) - (2^(10 - p) + z).
+template <int BITS>
+__device__ __forceinline__ h2_t qz_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
+                                        const uint32_t (&mgp)[Unit<BITS>::NPOS],
+                                        const PConsts<BITS>& c) {
   using U = Unit<BITS>;
   const int i = U::pidx(U::pos(s));
-  const h2_t m = as_h2(U::magic(w, s, mg));
-  return (m - c.hz[i]) * c.hs[POS ? 0 : i];
+  return as_h2(U::magic(w, s, mgp[i])) - c.hz[i];
+}
+
+// A value v of the exact per-code path as two fp16 numbers: its fp16
+// rounding hi and the remainder lo = fp16(v - hi) (exact when v is an
+// integer below 2^22 in magnitude, or an fp32 product of one with an fp16).
+__device__ __forceinline__ void split_f16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_h_bits(v);
+  lo = f32_to_h_bits(v - h_bits_to_f32(hi));
 }
 
 // Where a unit's codes live in the row.  4-bit / 2-bit units are one run of
@@ -348,64 +310,10 @@ __device__ __forceinline__ int unit_k(const UnitRef& u, int c) {
   return u.ka + c;
 }
 
-// Load one unit's words of one row (zeros where the segment is outside).
-template <int BITS>
-__device__ __forceinline__ void load_unit(const uint32_t* __restrict__ rowp, const UnitRef& u,
-                                          uint32_t (&w)[Unit<BITS>::WORDS]) {
-  if constexpr (BITS == 3) {
-    const uint32_t* pa = rowp + 3 * (u.ka >> 5);
-    const uint32_t* pb = rowp + 3 * (u.kb >> 5);
-    w[0] = u.va ? pa[0] : 0u;
-    w[1] = u.va ? pa[1] : 0u;
-    w[2] = u.va ? pa[2] : 0u;
-    w[3] = u.vb ? pb[0] : 0u;
-    w[4] = u.vb ? pb[1] : 0u;
-    w[5] = u.vb ? pb[2] : 0u;
-  } else {
-    const uint4 v = u.va ? *reinterpret_cast<const uint4*>(rowp + (u.ka * BITS >> 5))
-                         : make_uint4(0u, 0u, 0u, 0u);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
-  }
-}
-
-// Quantization parameters of constant set `cs` of a unit (per-group layout).
 // Group index of input channel k: a shift when the group size is a power of
 // two (gshift >= 0), a division otherwise.
 __device__ __forceinline__ int group_of(int k, int gsz, int gshift) {
   return gshift >= 0 ? (k >> gshift) : k / gsz;
-}
-
-template <int BITS>
-__device__ __forceinline__ HalfParams load_params(const uint16_t* __restrict__ srow,
-                                                  const int32_t* __restrict__ zrow, int gsz,
-                                                  int gshift, const UnitRef& u, int cs) {
-  HalfParams hp;
-  int kl, kh;
-  bool vl, vh;
-  if constexpr (BITS == 3) {
-    kl = u.ka;
-    kh = u.kb;
-    vl = u.va;
-    vh = u.vb;
-  } else if constexpr (BITS == 2) {
-    kl = kh = u.ka + 32 * cs;
-    vl = vh = u.va;
-  } else {
-    kl = kh = u.ka;
-    vl = vh = u.va;
-  }
-  const int gl = vl ? group_of(kl, gsz, gshift) : 0;
-  const int gh = vh ? group_of(kh, gsz, gshift) : 0;
-  hp.s_lo = srow[gl];
-  hp.z_lo = zrow[gl];
-  hp.s_hi = srow[gh];
-  hp.z_hi = zrow[gh];
-  hp.v_lo = vl;
-  hp.v_hi = vh;
-  return hp;
 }
 
 // One 16-byte activation entry: the four slots of quad q of a unit, each an
