@@ -236,13 +236,18 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
-        } else if constexpr (GM == kWideGroups) {
+        }
+      }
+      if constexpr (GM == kWideGroups) {
+        // one group per run of units
+#pragma unroll
+        for (int u = 0; u < NWMAX; ++u)
           if (run_start(u) == u) {
+            const UnitRef ur = my_unit(t, u < NW ? u : 0);
 #pragma unroll
             for (int c = 0; c < NC; ++c)
               b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
           }
-        }
       }
     };
 
@@ -343,9 +348,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
           const int m0 = (kp * NW + u) * Q;
           const uint4* xe = xs + (m0 * BT) * 64 + h * 16;
           f4_t at[BT];  // wide groups: this unit's sums, scaled into acc below
-#pragma unroll
-          for (int bt = 0; bt < BT; ++bt) at[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          auto mma = [&](int s, const h2_t (&d)[4]) {
+          // fresh: the unit's first MFMA starts at[] from zero
+          auto mma = [&](int s, const h2_t (&d)[4], bool fresh) {
             const h8_t bv = __builtin_bit_cast(
                 h8_t, make_uint4(as_u32(d[0]), as_u32(d[1]), as_u32(d[2]), as_u32(d[3])));
 #pragma unroll
@@ -353,7 +357,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
               const h8_t av =
                   __builtin_bit_cast(h8_t, xe[(s * BT + bt) * 64 + (i16 ^ ((m0 + s) & 15))]);
               if constexpr (GM == kWideGroups)
-                at[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, at[bt], 0, 0, 0);
+                at[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    av, bv, fresh ? f4_t{0.0f, 0.0f, 0.0f, 0.0f} : at[bt], 0, 0, 0);
               else
                 acc[bt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bt], 0, 0, 0);
             }
@@ -375,10 +380,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
                   hi[e] = qz[e] * s2;
                   lo[e] = __builtin_elementwise_fma(qz[e], s2, -hi[e]);
                 }
-                mma(s, hi);
-                mma(s, lo);
+                mma(s, hi, false);
+                mma(s, lo, false);
               } else {
-                mma(s, qz);
+                mma(s, qz, s == 0);
               }
             }
           } else {
@@ -390,6 +395,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
             uint32_t* wsc = slow_scratch + wave * (W * 64);
 #pragma unroll
             for (int i = 0; i < W; ++i) wsc[i * 64 + lane] = b.w[u][i];
+#pragma unroll
+            for (int bt = 0; bt < BT; ++bt) at[bt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
             for (int s = 0; s < Q; ++s) {
               h2_t hi[4], lo[4];
@@ -409,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
                 hi[e] = as_h2((uint32_t)hl | ((uint32_t)hh16 << 16));
                 lo[e] = as_h2((uint32_t)ll | ((uint32_t)lh << 16));
               }
-              mma(s, hi);
-              mma(s, lo);
+              mma(s, hi, false);
+              mma(s, lo, false);
             }
           }
           if constexpr (GM == kWideGroups) {

@@ -264,13 +264,26 @@ template <int BITS>
 __device__ __forceinline__ bool make_pconsts(const HalfParams& hp, PConsts<BITS>& c,
                                              bool direct) {
   using U = Unit<BITS>;
+  // zero points in [0, 2^(10 - PMAX)) -- those of every group whose range
+  // contains 0 -- by integer operations: 2^(10 - p) + z is then the pattern
+  // (25 - p) << 10 plus z << p; others by conversion (wave-uniform branch)
+  const uint32_t zmax = 1024u >> U::PMAX;
+  if (__all((uint32_t)hp.z_lo < zmax && (uint32_t)hp.z_hi < zmax)) {
+    const uint32_t z2 = ((uint32_t)hp.z_lo & 0xffffu) | ((uint32_t)hp.z_hi << 16);
 #pragma unroll
-  for (int p = 0; p <= U::PMAX; ++p) {
-    if (!U::uses(p)) continue;
-    const float base = (float)(1 << (10 - p));
-    const uint32_t lo = f32_to_h_bits(base + (float)hp.z_lo);
-    const uint32_t hi = BITS == 3 ? f32_to_h_bits(base + (float)hp.z_hi) : lo;
-    c.hz[U::pidx(p)] = as_h2(lo | (hi << 16));
+    for (int p = 0; p <= U::PMAX; ++p) {
+      if (!U::uses(p)) continue;
+      c.hz[U::pidx(p)] = as_h2((uint32_t)(25 - p) * 0x04000400u + (z2 << p));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p <= U::PMAX; ++p) {
+      if (!U::uses(p)) continue;
+      const float base = (float)(1 << (10 - p));
+      const uint32_t lo = f32_to_h_bits(base + (float)hp.z_lo);
+      const uint32_t hi = BITS == 3 ? f32_to_h_bits(base + (float)hp.z_hi) : lo;
+      c.hz[U::pidx(p)] = as_h2(lo | (hi << 16));
+    }
   }
   c.s2 = as_h2((uint32_t)hp.s_lo | ((uint32_t)hp.s_hi << 16));
   bool ok = hp.z_lo >= -1024 && hp.z_lo <= 1024 && hp.z_hi >= -1024 && hp.z_hi <= 1024;
