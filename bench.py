@@ -306,7 +306,7 @@ def cpu_baseline(budget_s: float = 12.0) -> dict:
             "kind": "oracle",
             "sample": f"{rows_done} weight rows ({rows_per_chunk}-row chunks alternating the "
                       f"12288x12288 and 49152x12288 layers' shape, K=12288, 3-bit per-row) through "
-                      f"the oracle's unpack + exact fp16 dequant + fp64 product, batch 1; "
+                      f"the oracle's unpack + exact dequantization + fp64 product, batch 1; "
                       f"{t_total:.1f} s single-threaded"}
 
 

@@ -17,18 +17,16 @@
 // the low and high fp16 halves of one 32-bit register, so that the fp16 math
 // runs two codes per instruction.  A slot's code field sits at bit position p
 // of both halves (3-bit: windows of ten codes are first cut out of the
-// straddling words with funnel shifts and byte permutes).  Masked out alone,
-// under a zero exponent field, the field is the exact fp16 subnormal
-// q * 2^(p - 24) (the matrix-vector kernel's decode); OR-ed into the fp16
-// pattern of 2^(10 - p) it is the exact fp16 integer 2^(10 - p) + q, from
-// which one subtraction gives q - z exactly (the matrix-core kernel's).
+// straddling words with funnel shifts and byte permutes).  OR-ed into the
+// fp16 pattern of 2^(10 - p), the field is the exact fp16 integer
+// 2^(10 - p) + q, from which one packed subtraction gives q - z exactly.
 //
 // The activations are stored on chip in the same slot order, so no
 // per-weight shuffle is needed in the inner loop.
 //
 // 8-bit codes have no room for a shift (p = 0 for every slot): each slot
 // pairs two neighbouring bytes of one word, which one byte permute places in
-// the two halves, under zero bytes or under the 0x64 exponent bytes of 1024.
+// the two halves, under the 0x64 exponent bytes of 1024.
 #pragma once
 
 #include "common.h"
@@ -154,7 +152,7 @@ struct Unit<8> {
   static constexpr int NPOS = 1;
   __host__ __device__ static constexpr int pidx(int) { return 0; }
   // v_perm_b32 selectors 0..3 pick bytes of the word, 4..7 bytes of mg, whose
-  // bytes 1 and 3 become the halves' high bytes (0x64: 1024 + q; 0: q * 2^-24)
+  // bytes 1 and 3 (0x64) become the halves' high bytes: 1024 + q
   __device__ static __forceinline__ uint32_t magic(const uint32_t (&w)[WORDS], int s,
                                                     uint32_t mg) {
     return __builtin_amdgcn_perm(mg, w[s >> 1], (s & 1) ? 0x07030502u : 0x07010500u);
