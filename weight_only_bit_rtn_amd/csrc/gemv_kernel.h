@@ -64,7 +64,7 @@ constexpr int kWaves = 16;                 // one 1024-thread workgroup per CU
 constexpr int kThreads = kWaves * kWave;
 constexpr size_t kLdsBudget = 160 * 1024;   // gfx950 LDS per CU
 constexpr int kPartMax = 4096;              // fp32 partial sums per round
-constexpr int kItemsPerWave = 4;            // target work items per wave
+constexpr int kItemsPerWave = 2;            // target work items per wave
 constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
 constexpr int kSlc = 2;  // buffer-load cache policy for the weights: streaming
 
