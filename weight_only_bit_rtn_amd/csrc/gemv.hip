@@ -1,8 +1,9 @@
 // gemv.hip -- dispatch of the dequant-GEMV by bit width and batch size.
 //
-// Batches 1..8 run on the VALU kernel (gemv_kernel.h).  From 9 rows on, and
-// whenever the activations do not fit the on-chip staging budget, the
-// product goes to the matrix-core kernel (gemm.hip): at those batch sizes the
+// Batches 1..8 run on the VALU kernel (gemv_kernel.h), in passes of four
+// rows when the activations of all rows do not fit the on-chip staging
+// budget.  From 9 rows on, and when even four rows do not fit, the product
+// goes to the matrix-core kernel (gemm.hip): at those batch sizes the
 // per-weight work is dominated by the batch-many multiply-adds, which the
 // fp16 MFMA units do for free while the VALU only decodes.
 #include "kernels.h"
@@ -15,6 +16,30 @@ hipError_t launch_qgemv_bits(const uint16_t* x, int B, const uint32_t* packed,
                              int gsz, int gshift, bool meta, uint16_t* y, hipStream_t stream);
 
 constexpr int kGemvMaxValuBatch = 8;
+constexpr int kGemvPassBatch = 4;  // rows per pass when all rows do not fit on chip
+
+namespace {
+
+hipError_t launch_rows(const uint16_t* x, int B, const uint32_t* packed, const uint16_t* scales,
+                       const int32_t* zeros, int N, int K, int G, int gsz, int gshift, int bits,
+                       bool meta, uint16_t* y, hipStream_t stream) {
+  switch (bits) {
+    case 2:
+      return launch_qgemv_bits<2>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, meta, y,
+                                  stream);
+    case 3:
+      return launch_qgemv_bits<3>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, meta, y,
+                                  stream);
+    case 8:
+      return launch_qgemv_bits<8>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, meta, y,
+                                  stream);
+    default:
+      return launch_qgemv_bits<4>(x, B, packed, scales, zeros, N, K, G, gsz, gshift, meta, y,
+                                  stream);
+  }
+}
+
+}  // namespace
 
 hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
@@ -25,20 +50,20 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
   const int G = (int)(K / gsz);
   const int gshift = (gsz & (gsz - 1)) == 0 ? __builtin_ctz((unsigned)gsz) : -1;
   const int b = (int)B, n = (int)N, k = (int)K;
-  switch (bits) {
-    case 2:
-      return launch_qgemv_bits<2>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
-                                  stream);
-    case 3:
-      return launch_qgemv_bits<3>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
-                                  stream);
-    case 8:
-      return launch_qgemv_bits<8>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
-                                  stream);
-    default:
-      return launch_qgemv_bits<4>(x, b, packed, scales, zeros, n, k, G, gsz, gshift, meta, y,
-                                  stream);
+  hipError_t e = launch_rows(x, b, packed, scales, zeros, n, k, G, gsz, gshift, bits, meta, y,
+                             stream);
+  if (e != hipErrorNotSupported || b <= kGemvPassBatch) return e;
+  // The activations of all rows do not fit on chip: passes of up to four rows
+  // (the weights are read once per pass, which costs less than the matrix-core
+  // path at these batch sizes).  Every pass has the on-chip needs of the first
+  // or fewer, so either the first is refused and nothing runs, or all run.
+  for (int b0 = 0; b0 < b; b0 += kGemvPassBatch) {
+    const int bc = b - b0 < kGemvPassBatch ? b - b0 : kGemvPassBatch;
+    e = launch_rows(x + (int64_t)b0 * K, bc, packed, scales, zeros, n, k, G, gsz, gshift, bits,
+                    meta, y + (int64_t)b0 * N, stream);
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace lowbit
