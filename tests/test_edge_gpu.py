@@ -242,11 +242,12 @@ def test_qgemm_shapes(lw, bits, N, K, g):
     _check_product(lw, w, bits, g, [1, 16, 17, 33, 64, 70], "qgemm")
 
 
-# Groups at least as long as one lane's units of a matrix-core step (2- and
-# 4-bit, g >= 128), with K not a multiple of the 512-long step: the last step
-# of every row runs past the row end.
+# Groups that hold a matrix-core step's unit spans whole (4-bit g >= 128,
+# 2-bit g >= 256; the 2-bit g = 128 cases take the two-operand form), with K
+# not a multiple of the 512-long step: the last step of every row runs past
+# the row end.
 WIDE_GROUP_CASES = [(4, 33, 640, 128), (4, 17, 1280, 256), (2, 9, 640, 128), (2, 21, 1408, 128),
-                    (4, 40, 2176, 128)]
+                    (4, 40, 2176, 128), (2, 19, 1280, 256)]
 
 
 @pytest.mark.parametrize("bits,N,K,g", WIDE_GROUP_CASES)
@@ -267,6 +268,21 @@ def test_products_degenerate(lw, kind, bits):
     for g in (0, 64):
         _check_product(lw, w, bits, g, [1, 4], "qgemv", stress)
         _check_product(lw, w, bits, g, [16, 40], "qgemm", stress)
+
+
+@pytest.mark.parametrize("kind", ["wide", "offset", "tiny", "negative"])
+@pytest.mark.parametrize("bits,g", [(4, 128), (4, 256), (2, 256)])
+def test_products_wide_groups_degenerate(lw, kind, bits, g):
+    """The matrix-core layout that scales each unit's sum (groups holding
+    the unit spans whole), on weights whose zero points fall outside
+    +-1024 (offset) or whose scales are large or tiny: the exact per-code
+    path inside that layout."""
+    N, K = 37, 4096
+    _say(f"[wide degenerate] kind={kind} bits={bits} g={g}")
+    w = _weights(kind, N, K, seed=5 * bits + g)
+    stress = kind in ("wide", "offset")
+    _check_product(lw, w, bits, g, [16, 40, 64], "qgemm", stress)
+    _check_product(lw, w, bits, g, [1, 4], "qgemv", stress)
 
 
 def test_products_are_deterministic(lw):
