@@ -195,6 +195,42 @@ struct RowParams {
       z = zeros + n * G;
     }
   }
+  // NV = 2 or 4 consecutive groups g .. g + NV - 1 with one vector load per
+  // array (the caller keeps g and the row's group count multiples of NV, so
+  // the loads are naturally aligned and stay inside the row)
+  template <int NV>
+  __device__ __forceinline__ void at_vec(int g, uint16_t (&sb)[NV], int32_t (&zz)[NV]) const {
+    static_assert(NV == 2 || NV == 4, "two or four groups");
+    uint32_t wv[NV];
+    if constexpr (META) {
+      if constexpr (NV == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(m + g);
+        wv[0] = v.x, wv[1] = v.y, wv[2] = v.z, wv[3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(m + g);
+        wv[0] = v.x, wv[1] = v.y;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        sb[i] = (uint16_t)wv[i];
+        zz[i] = (int32_t)wv[i] >> 16;
+      }
+    } else {
+      if constexpr (NV == 4) {
+        const uint2 sv = *reinterpret_cast<const uint2*>(s + g);
+        const int4 zv = *reinterpret_cast<const int4*>(z + g);
+        wv[0] = sv.x, wv[1] = sv.x >> 16, wv[2] = sv.y, wv[3] = sv.y >> 16;
+        zz[0] = zv.x, zz[1] = zv.y, zz[2] = zv.z, zz[3] = zv.w;
+      } else {
+        const uint32_t sv = *reinterpret_cast<const uint32_t*>(s + g);
+        const int2 zv = *reinterpret_cast<const int2*>(z + g);
+        wv[0] = sv, wv[1] = sv >> 16;
+        zz[0] = zv.x, zz[1] = zv.y;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) sb[i] = (uint16_t)wv[i];
+    }
+  }
   __device__ __forceinline__ void at(int g, uint16_t& sb, int32_t& zz) const {
     if constexpr (META) {
       const uint32_t v = m[g];
