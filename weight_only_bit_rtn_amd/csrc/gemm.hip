@@ -89,7 +89,7 @@ template <int BITS, int BT, int GM, bool META>
 __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     const uint16_t* __restrict__ x, int B, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
-    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift) {
+    uint16_t* __restrict__ y, int N, int K, int G, int gsz, int gshift, int pstage) {
   using U = Unit<BITS>;
   constexpr int Q = U::QUADS, W = U::WORDS, NC = U::NCONST;
   constexpr bool PERROW = GM == kPerRow;
@@ -105,9 +105,18 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   // layouts whose groups do not hold every MFMA's units whole
   constexpr bool DIRECT = GM == kPow2Groups || GM == kAnyGroups;
   // LDS: two activation tiles (later the partial sums), then per-wave scratch
-  // of the exact decode path
+  // of the exact decode path, then (wide groups, when the host asks for it)
+  // each wave's copy of its 16 rows' scales and zeros
   extern __shared__ uint4 lds[];
   uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(lds + 2 * XBUF);
+  // staged parameters, in 32-bit words: a row's G scales (fp16 pairs) at
+  // stride ssw, its G zeros (or compact words) at stride zsw; the padding
+  // spreads the 16 rows of one read over the banks
+  // (batch tiles of 64 rows leave too little LDS, and the code would cost
+  // them registers, so they never stage)
+  constexpr bool kStage = GM == kWideGroups && BT <= 2;
+  const int ssw = G / 2 + 2, zsw = G + 4;
+  const int pww = META ? 16 * zsw : 16 * (ssw + zsw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -151,6 +160,35 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     const uint32_t row_off = (uint32_t)i16 * row_bytes;
     // META: `scales` holds compact words (see RowParams), `zeros` is unused
     const RowParams<META> rp(scales, zeros, n, G);
+
+    // Wide groups: the wave copies its 16 rows' scales and zeros into LDS
+    // once per round (one contiguous read per row), so the steps read them
+    // from LDS instead of issuing one more global load per parameter array
+    // and step; rows past N take row N - 1, whose outputs are not written.
+    // The host asks for this only when G is a multiple of 8, the arrays are
+    // 16-byte aligned and the copy fits the LDS.
+    uint32_t* pw = slow_scratch + kWaves * W * 64 + wave * pww;
+    if constexpr (kStage) {
+      if (pstage) {
+        const int sc = META ? G / 4 : G / 8;  // 16-byte chunks of a row's first array
+        for (int e = lane; e < 16 * sc; e += 64) {
+          const int r = e / sc, c = e - r * sc;
+          const int64_t nr = min(16 * grp + r, N - 1);
+          const uint4 v = *reinterpret_cast<const uint4*>(scales + (nr * G + (META ? 4 : 8) * c) * (META ? 2 : 1));
+          uint32_t* d = pw + r * (META ? zsw : ssw) + 4 * c;
+          d[0] = v.x, d[1] = v.y, d[2] = v.z, d[3] = v.w;
+        }
+        if constexpr (!META) {
+          const int zc = G / 4;
+          for (int e = lane; e < 16 * zc; e += 64) {
+            const int r = e / zc, c = e - r * zc;
+            const int64_t nr = min(16 * grp + r, N - 1);
+            const int4 v = *reinterpret_cast<const int4*>(zeros + nr * G + 4 * c);
+            *reinterpret_cast<int4*>(pw + 16 * ssw + r * zsw + 4 * c) = v;
+          }
+        }
+      }
+    }
 
     // per-row constants (one group per row): computed once per round; the
     // row's scale multiplies the finished sum
@@ -253,7 +291,39 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
         if (wide_vec && g0 + NVMAX <= G) {
           uint16_t sv[NVMAX];
           int32_t zv[NVMAX];
-          rp.template at_vec<NVMAX>(g0, sv, zv);
+          if (kStage && pstage) {
+            uint32_t wv[NVMAX];
+            if constexpr (META) {
+              const uint32_t* mp = pw + i16 * zsw + g0;
+              if constexpr (NVMAX == 4) {
+                const uint4 v = *reinterpret_cast<const uint4*>(mp);
+                wv[0] = v.x, wv[1] = v.y, wv[2] = v.z, wv[3] = v.w;
+              } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(mp);
+                wv[0] = v.x, wv[1] = v.y;
+              }
+#pragma unroll
+              for (int i = 0; i < NVMAX; ++i) zv[i] = (int32_t)wv[i] >> 16;
+            } else {
+              const uint32_t* sp = pw + i16 * ssw + g0 / 2;
+              const int32_t* zp = reinterpret_cast<const int32_t*>(pw + 16 * ssw + i16 * zsw + g0);
+              if constexpr (NVMAX == 4) {
+                const uint2 v = *reinterpret_cast<const uint2*>(sp);
+                wv[0] = v.x, wv[1] = v.x >> 16, wv[2] = v.y, wv[3] = v.y >> 16;
+                const int4 z4 = *reinterpret_cast<const int4*>(zp);
+                zv[0] = z4.x, zv[1] = z4.y, zv[2] = z4.z, zv[3] = z4.w;
+              } else {
+                const uint32_t v = *sp;
+                wv[0] = v, wv[1] = v >> 16;
+                const int2 z2 = *reinterpret_cast<const int2*>(zp);
+                zv[0] = z2.x, zv[1] = z2.y;
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < NVMAX; ++i) sv[i] = (uint16_t)wv[i];
+          } else {
+            rp.template at_vec<NVMAX>(g0, sv, zv);
+          }
 #pragma unroll
           for (int u = 0; u < NWMAX; ++u)
             if (run_start(u) == u) {
@@ -507,17 +577,34 @@ template <int BITS, int BT, int GM, bool META>
 hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
-  const size_t lds = 2 * (size_t)kTileK * 16 * BT * 2 + (size_t)kWaves * Unit<BITS>::WORDS * 64 * 4;
+  size_t lds = 2 * (size_t)kTileK * 16 * BT * 2 + (size_t)kWaves * Unit<BITS>::WORDS * 64 * 4;
   if (lds > device_lds_per_block()) return hipErrorNotSupported;
+  // wide groups whose group is exactly one step's run span: stage each
+  // wave's scales and zeros in LDS when they fit (the kernel's layout:
+  // strides G/2 + 2 and G + 4 words per row, 16 rows per wave)
+  int pstage = 0;
+  if (GM == kWideGroups && BT <= 2) {
+    const int span = 4 * (BITS == 8 ? 2 : 1) * Unit<BITS>::CODES;
+    const size_t pww = META ? 16 * (size_t)(G + 4) : 16 * (size_t)(G / 2 + 2 + G + 4);
+    const size_t extra = (size_t)kWaves * pww * 4;
+    const bool aligned = reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
+                         (META || reinterpret_cast<uintptr_t>(zeros) % 16 == 0);
+    if (gsz == span && G % 8 == 0 && aligned && lds + extra <= device_lds_per_block()) {
+      pstage = 1;
+      lds += extra;
+    }
+  }
   const auto kern = qgemm_kernel<BITS, BT, GM, META>;
-  // the LDS request exceeds the default limit: raise it once per device
-  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern), (int)lds);
+  // the LDS request exceeds the default limit: raise it, once per device, to
+  // the most any launch of this kernel can ask for
+  const hipError_t e =
+      raise_lds_limit(reinterpret_cast<const void*>(kern), (int)device_lds_per_block());
   if (e != hipSuccess) return e;
   const int NG = (N + 15) / 16;
   const int cus = device_cu_count();
   const int grid = NG < cus ? NG : cus;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, x, B, packed, scales, zeros,
-                     y, N, K, G, gsz, gshift);
+                     y, N, K, G, gsz, gshift, pstage);
   return hipGetLastError();
 }
 
