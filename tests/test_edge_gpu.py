@@ -259,6 +259,37 @@ def test_products_wide_groups_ragged(lw, bits, N, K, g, kind):
     _check_product(lw, w, bits, g, [1, 4], "qgemv")
 
 
+# At least five 16-row groups per workgroup (on 256 CUs), so a whole 512-k
+# step sits in one K part, and G a multiple of 8, with the group exactly a
+# step run's span: at batch tiles of 16 and 32 rows the matrix-core product
+# copies each wave's scales and zeros into LDS and reads them there, while the
+# 64-row tile loads them per step.  Every output row must come out with the
+# same bits either way, and the same as from the compact group words.
+STAGED_CASES = [(4, 20487, 1024, 128), (8, 20487, 1024, 128), (2, 20487, 2048, 256)]
+
+
+@pytest.mark.parametrize("bits,N,K,g", STAGED_CASES)
+def test_qgemm_staged_group_parameters(lw, bits, N, K, g):
+    import torch
+    _say(f"[staged parameters] bits={bits} N={N} K={K} g={g}")
+    w = _weights("mixed", N, K, seed=N + 13 * K + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    p, s, z = _to_gpu(packed), _to_gpu(scales), _to_gpu(zeros)
+    meta = lw.pack_meta(s, z)
+    x = harness.synth.normal_f16(48, K, 1.0, seed=17, stream=2)
+    xg = _to_gpu(x)
+    y48 = lw.qgemm(xg, p, s, z, K, bits, g)
+    for B in (16, 32):
+        xb = xg[:B].contiguous()
+        yb = lw.qgemm(xb, p, s, z, K, bits, g)
+        ym = lw.qgemm_meta(xb, p, meta, K, bits, g)
+        torch.cuda.synchronize()
+        assert torch.equal(yb.view(torch.int16), y48[:B].view(torch.int16)), f"B={B} vs B=48"
+        assert torch.equal(ym.view(torch.int16), yb.view(torch.int16)), f"B={B} compact words"
+    y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g)
+    harness.assert_y_close(y48.cpu().numpy(), y_ref, f"qgemm bits={bits} N={N} K={K} g={g} B=48")
+
+
 @pytest.mark.parametrize("kind", ["wide", "tiny", "offset", "mixed", "positive", "negative", "ties"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_products_degenerate(lw, kind, bits):
