@@ -17,8 +17,9 @@ launch stream around the timed region (elapsed / launches).  The quantizer
 (lowbit_quantize_rtn, and lowbit_quantize_rtn_sym for the signed symmetric
 grid), every workload's products and the matrix-core product (lowbit_qgemm,
 Llama-70B MLP shape at batch 16/32/64) are measured in the same run as
-separate stages.  The CPU baseline times the C oracle's dequantize + fp64
-product on a sample of rows of the same layers.
+separate stages.  The CPU baseline times the C oracle (unpack + exact
+dequantization + fp64 product, and quantize + pack) on bounded samples of the
+same layers, single-threaded and with rows split over the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
                        [--no-stages] [--stage-reps 20] [--gptq-only] [--counter-pass]
@@ -43,6 +44,7 @@ FP64_PEAK_TFLOPS = 78.6         # MI355X fp64 (vector and matrix), published
 MALL_DEFEAT_BYTES = 1 << 30
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "qgemv_opt175b_3bit_traffic.json")
 GEMV_SOURCES = ["gemv.hip", "gemv3.hip", "gemv_kernel.h", "unit_decode.h", "common.h"]
+GEMV_KERNEL = "qgemv_kernel<3,1,R,perrow>"
 
 
 def log(msg: str) -> None:
@@ -145,6 +147,12 @@ WIDE_LAYERS = (("opt175b_fc1_49152x12288_8bit", 49152, 12288, 8, 0, (1, 4)),
                ("llama70b_up_28672x8192_8bit", 28672, 8192, 8, 128, (16, 32, 64)))
 
 
+# One GPU's share of the OPT-175B fc1 layer when it is split by output rows
+# over two GPUs (the OPTQ card's 3-bit OPT-175B run on two GPUs): the same
+# kernel on half the rows.
+SHARD_LAYERS = (("opt175b_fc1_shard_24576x12288", 24576, 12288, 3, 0, (1,)),)
+
+
 # Error-feedback (GPTQ) quantization, fp64: (layer name, calibration rows).
 GPTQ_LAYERS = (("outlier_2048", 2048), ("llama7b_up_11008x4096", 4096))
 
@@ -198,6 +206,7 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     import synth
     stages = {}
     wide = [synth.Layer(*spec) for spec in WIDE_LAYERS]
+    shard = [synth.Layer(*spec) for spec in SHARD_LAYERS]
     # quantize + pack (reads 2 B per weight): the OPT-175B 3-bit per-row
     # layers and the Llama-70B 4-bit layer (groups of 128), on the min-max
     # grid and, for the larger two, on the signed symmetric grid
@@ -230,7 +239,7 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
         del w, packed, scales, zeros
         torch.cuda.empty_cache()
     # every workload's products
-    for name, layers in list(synth.WORKLOADS.items()) + [("8bit", wide)]:
+    for name, layers in list(synth.WORKLOADS.items()) + [("shard", shard), ("8bit", wide)]:
         for layer in layers:
             prep = None
             # grouped layers are also timed with compact group words
@@ -277,37 +286,79 @@ def measure_stages(lw, torch, stream: int, reps: int) -> dict:
     return stages
 
 
-def cpu_baseline(budget_s: float = 12.0) -> dict:
-    """The C oracle (single-threaded) on a bounded sample of the same layers."""
-    import numpy as np
+def _oracle_rate(work, nbytes: int, threads: int, budget_s: float):
+    """Run work() repeatedly on `threads` Python threads (the oracle's C calls
+    release the GIL) for about budget_s seconds of wall time; returns
+    (bytes per second, calls, seconds)."""
+    import threading
+    calls = [0] * threads
+    t0 = time.perf_counter()
+    t_end = t0 + budget_s
+
+    def loop(i: int) -> None:
+        while True:
+            work(i)
+            calls[i] += 1
+            if time.perf_counter() >= t_end:
+                return
+
+    ts = [threading.Thread(target=loop, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    wall = time.perf_counter() - t0
+    return sum(calls) * nbytes / wall, sum(calls), wall
+
+
+def cpu_baseline(budget_s: float = 5.0) -> dict:
+    """The C oracle as it stands, on bounded samples of the metric's layers
+    (K = 12288, 3-bit, one group per row): the product (unpack + exact
+    dequantization + fp64 matrix-vector product, batch 1) and quantize + pack,
+    each single-threaded and with rows split over the host's cores."""
+    import numpy as np  # noqa: F401
 
     import oracle
     import synth
-    layers = synth.WORKLOADS["opt175b_3bit"]
-    rows_per_chunk = 256
-    nbytes = 0
-    rows_done = 0
-    t_total = 0.0
-    li = 0
-    while t_total < budget_s:
-        layer = layers[li % len(layers)]
-        li += 1
-        w = synth.normal_f16(rows_per_chunk, layer.K, layer.w_std, layer.seed + 1000 + li,
-                             synth.STREAM_W)
+    layer = synth.WORKLOADS["opt175b_3bit"][1]
+    rows = 256
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))   # the host's CPU share for one GPU
+    chunks = []
+    for i in range(cores):
+        w = synth.normal_f16(rows, layer.K, layer.w_std, layer.seed + 1000 + i, synth.STREAM_W)
         codes, scales, zeros = oracle.quantize_rtn(w, layer.bits, layer.group_size)
-        packed = oracle.pack(codes, layer.bits)
-        x = layer.activations(1)
-        t0 = time.perf_counter()
+        chunks.append((w, oracle.pack(codes, layer.bits), scales, zeros))
+    x = layer.activations(1)
+    pbytes = product_bytes(rows, layer.K, layer.bits, layer.group_size, 1)
+    qbytes = quantize_bytes(rows, layer.K, layer.bits, layer.group_size)
+
+    def product(i):
+        _, packed, scales, zeros = chunks[i % len(chunks)]
         oracle.reference_y(x, packed, scales, zeros, layer.K, layer.bits, layer.group_size)
-        t_total += time.perf_counter() - t0
-        nbytes += product_bytes(rows_per_chunk, layer.K, layer.bits, layer.group_size, 1)
-        rows_done += rows_per_chunk
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{rows_done} weight rows ({rows_per_chunk}-row chunks alternating the "
-                      f"12288x12288 and 49152x12288 layers' shape, K=12288, 3-bit per-row) through "
-                      f"the oracle's unpack + exact dequantization + fp64 product, batch 1; "
-                      f"{t_total:.1f} s single-threaded"}
+
+    def quantize(i):
+        w = chunks[i % len(chunks)][0]
+        codes, _, _ = oracle.quantize_rtn(w, layer.bits, layer.group_size)
+        oracle.pack(codes, layer.bits)
+
+    p1, n1, s1 = _oracle_rate(product, pbytes, 1, budget_s)
+    pn, nn, sn = _oracle_rate(product, pbytes, cores, budget_s)
+    q1, m1, t1 = _oracle_rate(quantize, qbytes, 1, budget_s)
+    qn, mn, tn = _oracle_rate(quantize, qbytes, cores, budget_s)
+    return {"value": round(pn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows}-row chunks of the {layer.N}x{layer.K} 3-bit per-row layer "
+                      f"(K={layer.K}), batch 1, through the oracle's unpack + exact "
+                      f"dequantization + fp64 product: {nn} chunks in {sn:.1f} s on {cores} "
+                      f"threads (rows split over the cores; {affinity} in the affinity mask)",
+            "single_thread": {"value": round(p1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "chunks": n1, "seconds": round(s1, 2)},
+            "quantize_pack": {"value": round(qn / 1e9, 4), "unit": "GB/s", "cores": cores,
+                              "chunks": mn, "seconds": round(tn, 2),
+                              "single_thread": round(q1 / 1e9, 4),
+                              "bytes_per_chunk": qbytes,
+                              "what": "oracle quantize_rtn + pack of the same chunks "
+                                      "(2 B read per weight + packed words + scales + zeros)"}}
 
 
 def load_traffic(avg_bytes_per_launch: int):
@@ -330,8 +381,9 @@ COPY_REF_BYTES = 1 << 30
 def counter_pass(lw, torch, layers, stream: int) -> int:
     """Launch sequence profiled by the counter passes (FETCH_SIZE, WRITE_SIZE,
     MfmaUtil / VALUBusy): the quantizer once per GEMV layer, three GEMV launches
-    per layer (distinct weight copies), two matrix-core launches per batch of
-    the Llama-70B MLP shape, then three plain device-to-device copies of
+    per layer (distinct weight copies), two GEMV launches per batch (1, 4, 8)
+    of each Llama-7B MLP layer, two matrix-core launches per batch of the
+    Llama-70B MLP shape, then three plain device-to-device copies of
     COPY_BYTES whose counter readings calibrate the bytes per count."""
     import synth
     preps = [Prepared(lw, torch, L, 3) for L in layers]  # quantizes each layer once
@@ -342,6 +394,17 @@ def counter_pass(lw, torch, layers, stream: int) -> int:
         for i in range(3):
             run_product(lw, p, 1, i, stream, "qgemv")
     torch.cuda.synchronize()
+    # the Llama-7B MLP layers, 2-bit groups of 64, at batch 1, 4 and 8
+    small = []
+    for L in synth.WORKLOADS["llama7b_mlp_2bit"]:
+        ps = Prepared(lw, torch, L, 2)
+        del ps.w
+        for B in L.batches:
+            for i in range(2):
+                run_product(lw, ps, B, i, stream, "qgemv")
+        torch.cuda.synchronize()
+        small.append(L)
+        del ps
     big = synth.WORKLOADS["llama70b_mlp_4bit"][0]
     pg = Prepared(lw, torch, big, 2)
     del pg.w
@@ -358,6 +421,9 @@ def counter_pass(lw, torch, layers, stream: int) -> int:
     torch.cuda.synchronize()
     per_launch = {p.layer.name: product_bytes(p.layer.N, p.layer.K, p.layer.bits,
                                               p.layer.group_size, 1) for p in preps}
+    for L in small:
+        for B in L.batches:
+            per_launch[f"{L.name}/B{B}"] = product_bytes(L.N, L.K, L.bits, L.group_size, B)
     for B in big.batches:
         per_launch[f"{big.name}/B{B}"] = product_bytes(big.N, big.K, big.bits, big.group_size, B)
     for p in preps:
@@ -443,12 +509,32 @@ def main() -> int:
     avg_bytes = step_bytes / launches
     achieved = avg_bytes / (avg_launch_ms * 1e-3) / 1e9
 
-    # per-layer device time, each launch bracketed by its own events (context)
-    per_layer = {}
-    for j, p in enumerate(preps):
-        avg, med = time_launches(torch, lambda i, p=p: run_product(lw, p, 1, i, stream, "qgemv"),
-                                 args.steps)
-        per_layer[p.layer.name] = (avg, med)
+    # per layer: the same back-to-back launches, one layer at a time, between
+    # one pair of events on the launch stream (the kernel trace's view), and
+    # each launch bracketed by its own events (median, p10, p90: launch
+    # overhead included)
+    per_layer, spread = {}, {}
+    for p in preps:
+        L = p.layer
+        for i in range(3):
+            run_product(lw, p, 1, i, stream, "qgemv")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            run_product(lw, p, 1, i, stream, "qgemv")
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        nb = product_bytes(L.N, L.K, L.bits, L.group_size, 1)
+        per_layer[L.name] = {"bytes_per_launch": nb, "avg_launch_us": round(us, 3),
+                             "achieved": round(nb / (us * 1e-6) / 1e9, 1),
+                             "frac": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        _, med, p10, p90 = time_launches(
+            torch, lambda i, p=p: run_product(lw, p, 1, i, stream, "qgemv"), args.steps,
+            spread=True)
+        spread[L.name] = {"median": round(med * 1e3, 2), "p10": round(p10 * 1e3, 2),
+                          "p90": round(p90 * 1e3, 2)}
     traffic = load_traffic(avg_bytes)
 
     result = {
@@ -469,13 +555,15 @@ def main() -> int:
                    "group_size": "per-row", "batch": 1, "weight_copies": copies,
                    "w_dist": "N(0,0.02) fp16", "x_dist": "N(0,1) fp16", "seed": 0},
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
-        "us_per_layer": {name: round(avg * 1e3, 2) for name, (avg, med) in per_layer.items()},
+        "us_per_layer": {name: rec["avg_launch_us"] for name, rec in per_layer.items()},
+        "us_per_launch_single": spread,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "qgemv_kernel<3,1,R,perrow>",
+                     "kernel": GEMV_KERNEL,
                      "bytes_per_launch": int(avg_bytes),
-                     "avg_launch_us": round(avg_launch_ms * 1e3, 3)},
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                     "layers": per_layer},
     }
     if not args.no_stages:
         log("[bench] stages")

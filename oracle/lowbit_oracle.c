@@ -20,9 +20,10 @@
  *    quantization, "block_wise_quant": S in R^{Ci/64 x Co}).
  *  - For b bits, M = 2^b - 1:  scale = (max - min) / M,  zero = round(-min/scale),
  *    q = clamp(round(w/scale) + zero, 0, M), with round-half-to-even.
- *  - Codes are packed several to a machine word ("two 4bits ... into one 8bit",
- *    "4x 2-bit weight in an uint8", "16 2-bits into an int32": [Feature
- *    Request] 4bit and 2bit and 1bit quantization support, comments).
+ *  - Several codes share one byte or one 32-bit word: two 4-bit codes per
+ *    byte, four 2-bit codes per byte, sixteen 2-bit codes per 32-bit word
+ *    ([Feature Request] 4bit and 2bit and 1bit quantization support,
+ *    comments).
  *  - At run time the low-bit weights are turned back into real values and
  *    multiplied against fp16 activations (same feature request, elephantpanda's
  *    comment on storing 4-bit weights and converting them with GPU cores);

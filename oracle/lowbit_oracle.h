@@ -15,7 +15,7 @@
  *   scales fp16 bit patterns  [N][G]   G = K / group_size (group_size 0 = per-row)
  *   zeros  int32              [N][G]
  *   x      fp16 bit patterns  [B][K]
- *   deq    fp16 bit patterns  [N][K]
+ *   deq    double             [N][K]   exact (q - zero) * scale, not rounded
  *   y      double             [B][N]
  * Every function returns 0 on success and -1 on a bad argument.
  */

@@ -74,6 +74,27 @@ def oracle_y(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.nd
     return out
 
 
+def oracle_gptq(w: np.ndarray, H: np.ndarray, bits: int, group_size: int,
+                symmetric: bool = False, parts: int | None = None):
+    """Oracle error-feedback codes of every row of w, with the rows split into
+    ``parts`` ranges run in parallel threads (rows are independent given H;
+    each call repeats the oracle's inverse-Hessian work for its range)."""
+    N, K = w.shape
+    G = oracle.groups(K, group_size)
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, G), np.float16)
+    zeros = np.empty((N, G), np.int32)
+
+    def run(rng):
+        r0, r1 = rng
+        c, s, z = oracle.quantize_gptq(w[r0:r1], H, bits, group_size, symmetric)
+        codes[r0:r1], scales[r0:r1], zeros[r0:r1] = c, s, z
+
+    with ThreadPoolExecutor(threads()) as ex:
+        list(ex.map(run, row_chunks(N, parts or threads())))
+    return codes, scales, zeros
+
+
 def oracle_abs_y(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
                  K: int, bits: int, group_size: int) -> np.ndarray:
     """sum_k |x[b][k] * deq[n][k]| (the size of the terms an output sums)."""

@@ -7,6 +7,9 @@
  *      symmetric divisors 2^(b-1) - 1 of b = 2, 3, 4, 8);
  *  (3) |w| / s < 2^22 for groups whose extrema lie within 8 fp16 steps of
  *      each other (where |w| / s is largest), so v + 1.5 * 2^23 rounds exactly.
+ * Usage: division_identity [STEP [PART PARTS]]: with PARTS > 1, check (1)
+ * covers only the scales whose index is PART modulo PARTS, so that PARTS
+ * processes together cover every STEP-th scale once.
  * Prints one line per check and exits non-zero on any failure. */
 #include <math.h>
 #include <stdint.h>
@@ -36,8 +39,12 @@ static uint16_t f2h(float f) { /* round to nearest even, finite values */
 
 int main(int argc, char** argv) {
   const int step = argc > 1 ? atoi(argv[1]) : 1;
+  const int part = argc > 3 ? atoi(argv[2]) : 0, parts = argc > 3 ? atoi(argv[3]) : 1;
+  if (step < 1 || parts < 1 || part < 0 || part >= parts) return 2;
   long bad = 0, n = 0;
+  long idx = -1;
   for (uint32_t sb = 1; sb < 0x7c00; sb += (uint32_t)step) {
+    if (++idx % parts != part) continue;
     const float s = h2f((uint16_t)sb);
     volatile float one = 1.0f;
     const float r_hi = one / s;

@@ -175,8 +175,8 @@ def test_products_8bit_degenerate(lw, kind):
             _check_products(lw, w, g, [16, 40], "qgemm", symmetric, stress, kind, x_std)
 
 
-# Two workload shapes at 8 bits, full size: every code bit-exact, products on
-# sampled rows, in the launch configurations the other widths use.
+# Two workload shapes at 8 bits, full size: every code bit-exact, every product
+# output in tolerance, in the launch configurations the other widths use.
 FULL = [synth.Layer("opt175b_attn_12288_8bit", 12288, 12288, 8, 0, (1,)),
         synth.Layer("llama70b_up_28672x8192_8bit", 28672, 8192, 8, 128, (1, 16, 64))]
 
@@ -188,7 +188,6 @@ def test_8bit_full_size(lw, layer):
     w = layer.weights()
     codes, scales, zeros, packed = _check_quantize(lw, w, layer.group_size, False, layer.name,
                                                    (False,))
-    rows = harness.sample_rows(layer.N)
     K, g = layer.K, layer.group_size
     args = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, BITS, g]
     for B in layer.batches:
@@ -196,5 +195,5 @@ def test_8bit_full_size(lw, layer):
         kernel = "qgemv" if B < 16 else "qgemm"
         y = getattr(lw, kernel)(_to_gpu(x), *args)
         torch.cuda.synchronize()
-        y_ref = harness.oracle_y(x, packed, scales, zeros, K, BITS, g, rows=rows)
-        harness.assert_y_close(y.cpu().numpy()[:, rows], y_ref, f"{layer.name} B={B}")
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, BITS, g)
+        harness.assert_y_close(y.cpu().numpy(), y_ref, f"{layer.name} B={B}")

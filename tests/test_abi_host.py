@@ -68,7 +68,7 @@ P = 0x7F0000000000
 MIS = P + 4
 
 
-@pytest.mark.parametrize("call,status", [
+HOST_VALIDATION_CASES = [
     # bit width
     (lambda lw: lw.quantize_rtn_raw(P, 4, 128, 5, 0, P, P, P, P, None), "UNSUPPORTED"),
     (lambda lw: lw.pack_raw(P, 4, 128, 1, P, None), "UNSUPPORTED"),
@@ -148,11 +148,17 @@ MIS = P + 4
     (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),
     (lambda lw: lw.qgemm_raw(None, 5, None, None, None, 0, 128, 4, 0, None, None), "OK"),
     (lambda lw: lw.pack_raw(None, 0, 128, 4, None, None), "OK"),
-])
-def test_host_validation(lw, call, status):
-    want = {"OK": lw.LOWBIT_OK, "ARG": lw.LOWBIT_ERR_ARG, "SHAPE": lw.LOWBIT_ERR_SHAPE,
+]
+
+
+def expected_status(lw, status: str) -> int:
+    return {"OK": lw.LOWBIT_OK, "ARG": lw.LOWBIT_ERR_ARG, "SHAPE": lw.LOWBIT_ERR_SHAPE,
             "UNSUPPORTED": lw.LOWBIT_ERR_UNSUPPORTED}[status]
-    assert call(lw) == want
+
+
+@pytest.mark.parametrize("call,status", HOST_VALIDATION_CASES)
+def test_host_validation(lw, call, status):
+    assert call(lw) == expected_status(lw, status)
 
 
 def test_binding_refuses_cpu_tensors(lw):

@@ -202,7 +202,7 @@ def test_sym_products(lw, bits, N, K, g):
 
 
 # The workload layer shapes, quantized on the symmetric grid at full size;
-# every row checked bit-exact, the products on sampled rows.
+# every row checked bit-exact, every output of the products in tolerance.
 SYM_LAYERS = [L for L in harness.all_layers() if L.name in (
     "outlier_2048", "llama7b_up_11008x4096", "llama70b_up_28672x8192",
     "opt175b_attn_12288")]
@@ -216,7 +216,6 @@ def test_sym_workload_layers(lw, layer):
     w = layer.weights()
     codes, scales, zeros, packed = _check_quantize(
         lw, w, layer.bits, layer.group_size, f"sym {layer.name}", (False,))
-    rows = harness.sample_rows(layer.N)
     K, bits, g = layer.K, layer.bits, layer.group_size
     args = [_to_gpu(packed), _to_gpu(scales), _to_gpu(zeros), K, bits, g]
     for B in layer.batches:
@@ -224,5 +223,5 @@ def test_sym_workload_layers(lw, layer):
         kernel = "qgemv" if B < 16 else "qgemm"
         y = getattr(lw, kernel)(_to_gpu(x), *args)
         torch.cuda.synchronize()
-        y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g, rows=rows)
-        harness.assert_y_close(y.cpu().numpy()[:, rows], y_ref, f"sym {layer.name} B={B}")
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g)
+        harness.assert_y_close(y.cpu().numpy(), y_ref, f"sym {layer.name} B={B}")

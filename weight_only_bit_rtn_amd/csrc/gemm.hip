@@ -187,6 +187,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
             *reinterpret_cast<int4*>(pw + 16 * ssw + r * zsw + 4 * c) = v;
           }
         }
+        // other lanes of this wave read these rows: order the LDS writes
+        // before their reads (a wave-scope release / acquire pair around a
+        // wave barrier; no workgroup barrier is needed, the slice is the
+        // wave's own)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
 

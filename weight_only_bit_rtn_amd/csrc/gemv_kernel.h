@@ -24,8 +24,8 @@
 // as two fp16 numbers.
 //
 // Work layout on gfx950:
-//  - one persistent workgroup of 16 waves per CU (the kernel claims the
-//    register budget of four waves per SIMD, so two never share a CU); x
+//  - one persistent workgroup of 16 waves per CU (each workgroup asks for
+//    more than half of the CU's LDS, so two never share a CU); x
 //    (all B rows, all K) is staged once per workgroup into LDS, already in
 //    the slot order the decode produces;
 //  - each workgroup owns an equal, contiguous share of the row tiles (R rows
@@ -63,6 +63,7 @@ namespace gemv_detail {
 constexpr int kWaves = 16;                 // one 1024-thread workgroup per CU
 constexpr int kThreads = kWaves * kWave;
 constexpr size_t kLdsBudget = 160 * 1024;   // gfx950 LDS per CU
+constexpr size_t kOneWgPerCuLds = kLdsBudget / 2 + 1024;  // above half a CU's LDS
 constexpr int kPartMax = 4096;              // fp32 partial sums per round
 constexpr int kItemsPerWave = 2;            // target work items per wave
 constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
@@ -161,11 +162,6 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   // LDS: activations [J][Q][BB][64] | per-wave scratch of the exact path |
   //      partial sums [RT * R rows][BB][JC] | work counter
   extern __shared__ uint4 xs[];
-
-  // Claim the whole register budget of four waves per SIMD, so that two of
-  // these 16-wave workgroups can never share a CU (the work split below
-  // assumes one workgroup per CU).
-  asm volatile("" ::: "v127");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -539,10 +535,14 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   int RT = kPartMax / (R * BB * JC);
   if (RT > tiles_per_wg) RT = tiles_per_wg;
   if (RT < 1) return hipErrorNotSupported;
-  const size_t lds = (size_t)J * U::QUADS * BB * 64 * sizeof(uint4) +
-                     (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) +
-                     (size_t)RT * R * BB * JC * sizeof(float) + 16;
+  size_t lds = (size_t)J * U::QUADS * BB * 64 * sizeof(uint4) +
+               (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) +
+               (size_t)RT * R * BB * JC * sizeof(float) + 16;
   if (lds > device_lds_per_block() || lds > kLdsBudget) return hipErrorNotSupported;
+  // Occupancy bound: the work split gives every workgroup an equal share of
+  // the rows and assumes one workgroup per CU.  A request above half of the
+  // CU's LDS makes that a hardware guarantee (a second workgroup never fits).
+  if (lds < kOneWgPerCuLds && kOneWgPerCuLds <= device_lds_per_block()) lds = kOneWgPerCuLds;
   const auto kern = qgemv_kernel<BITS, BB, R, PERROW, SPLIT, META>;
   if (lds > 64 * 1024) {
     // above the default limit: raise it (once per device) to the largest
