@@ -65,6 +65,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr size_t kLdsBudget = 160 * 1024;   // gfx950 LDS per CU
 constexpr size_t kOneWgPerCuLds = kLdsBudget / 2 + 1024;  // above half a CU's LDS
 constexpr int kPartMax = 4096;              // fp32 partial sums per round
+constexpr size_t kPartMaxMD = 16384;        // same, batch 1 with one group per row
 constexpr int kItemsPerWave = 2;            // target work items per wave
 constexpr int kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
 constexpr int kSlc = 2;  // buffer-load cache policy for the weights: streaming
@@ -131,7 +132,7 @@ struct Item {
   int c;       // K chunk
   int jb, je;  // K steps of the chunk
   int j;       // K step being loaded / computed
-  __amdgpu_buffer_rsrc_t rs[R];
+  const char* row[R];  // first byte of each row's packed words
 };
 
 // Separate sums a grouped unit needs: a 3-bit unit's two periods (low /
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   const int entries = J * Q * BB * 64;
   uint32_t* slow_scratch = reinterpret_cast<uint32_t*>(xs + entries);
   float* part = reinterpret_cast<float*>(slow_scratch + kWaves * W * 64);
-  int* counter = reinterpret_cast<int*>(part + RT * R * BB * JC);
+  int* counter = reinterpret_cast<int*>(part + RT * R * BB * JC * (MD ? 64 : 1));
 
   struct Buf {
     uint32_t w[R][W];
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const int n0 = (rt0 + t.tl) * R;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      t.rs[r] = rsrc(packed + (int64_t)min(n0 + r, N - 1) * (row_bytes / 4), row_bytes);
+      t.row[r] = reinterpret_cast<const char*>(packed + (int64_t)min(n0 + r, N - 1) * (row_bytes / 4));
     return t;
   };
   // Next (item, K step) of this wave: the next step of the same item, else a
@@ -224,8 +225,10 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
   auto load = [&](const Item<R>& t, Buf& b) {
     const int n0 = (rt0 + t.tl) * R;
     const int j = t.j;
+    // the K step enters through the descriptor (base + step, the rest of the
+    // row as its size: scalar arithmetic), so lanes past the row's end still
+    // read zeros and the lanes' offsets stay the same for every step
     const uint32_t step = (uint32_t)j * bytes_per_step<BITS>();
-    const uint32_t va_off = off_a + step, vb_off = off_b + step;
     // zero points (and for grouped rows the scales) before the words, so the
     // wait for the words also covers them
     if constexpr (PERROW) {
@@ -252,10 +255,10 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const auto rs = t.rs[r];
+      const auto rs = rsrc(t.row[r] + step, row_bytes - step);
       if constexpr (BITS == 3) {
-        const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, va_off, 0, kSlc);
-        const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, vb_off, 0, kSlc);
+        const u3_t va = __builtin_amdgcn_raw_buffer_load_b96(rs, off_a, 0, kSlc);
+        const u3_t vb = __builtin_amdgcn_raw_buffer_load_b96(rs, off_b, 0, kSlc);
         b.w[r][0] = va.x;
         b.w[r][1] = va.y;
         b.w[r][2] = va.z;
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         b.w[r][4] = vb.y;
         b.w[r][5] = vb.z;
       } else {
-        const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, va_off, 0, kSlc);
+        const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off_a, 0, kSlc);
         b.w[r][0] = v.x;
         b.w[r][1] = v.y;
         b.w[r][2] = v.z;
@@ -283,6 +286,8 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
 
   uint32_t mgp[U::NPOS];
   magic_registers<BITS>(mgp);
+  // lanes holding an element of the 16x16 accumulator's diagonal (see mfma_diag)
+  const bool diag_lane = ((lane & 15) >> 2) == (lane >> 4);
   PConsts<BITS> rowc[R];  // one group per row: the rows' constants (wave-uniform)
   int32_t row_z[R];
   bool rowfast = true;
@@ -299,10 +304,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           row_z[r] = (int32_t)uniform((uint32_t)b.z[r][0]);
-          const HalfParams h{0, 0, row_z[r], row_z[r], true, true};
-          rowfast &= make_pconsts<BITS>(h, rowc[r], false);
-#pragma unroll
-          for (int i = 0; i < U::NPOS; ++i) rowc[r].hz[i] = as_h2(uniform(as_u32(rowc[r].hz[i])));
+          rowfast &= row_pconsts<BITS>(row_z[r], rowc[r]);
         }
       }
 #pragma unroll
@@ -432,19 +434,36 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     }
 
     if (j == t.je - 1) {
-      // end of the item: one partial sum per (row, batch row) into LDS
+      // end of the item
+      if constexpr (MD) {
+        // The 16 lanes that hold the accumulator's diagonal store their four
+        // accumulator values (one LDS write each); the diagonal elements are
+        // picked and summed when the round's outputs are written.  An item
+        // that took the exact per-code path also has per-lane sums: they are
+        // reduced here and added to the diagonal element of lane 0.
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int bb = 0; bb < BB; ++bb) {
-          float v = acc[r][bb];
-          acc[r][bb] = 0.0f;
-          if constexpr (MD) {
-            v += mfma_diag(dacc[r], lane);
-            dacc[r] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r = 0; r < R; ++r) {
+          if (!rowfast) {
+            const float v = wave_sum_dpp(acc[r][0]);
+            if (lane == 0) dacc[r][0] += v;
           }
-          v = wave_sum_dpp(v);
-          if (lane == 0) part[((t.tl * R + r) * BB + bb) * JC + t.c] = v;
+          acc[r][0] = 0.0f;
+          if (diag_lane)
+            *reinterpret_cast<f4_t*>(part + ((t.tl * R + r) * JC + t.c) * 64 + 4 * (lane & 15)) =
+                dacc[r];
+          dacc[r] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      } else {
+        // one partial sum per (row, batch row) into LDS
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int bb = 0; bb < BB; ++bb) {
+            float v = acc[r][bb];
+            acc[r][bb] = 0.0f;
+            v = wave_sum_dpp(v);
+            if (lane == 0) part[((t.tl * R + r) * BB + bb) * JC + t.c] = v;
+          }
         }
       }
     }
@@ -498,9 +517,19 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
     const int nrows = min((rt0 + ntl) * R, N) - row0;
     for (int e = tid; e < nrows * BB; e += kThreads) {
       const int bb = e / nrows, rr = e - bb * nrows;
-      const float* pp = part + (rr * BB + bb) * JC;
       float v = 0.0f;
-      for (int c = 0; c < JC; ++c) v += pp[c];
+      if constexpr (MD) {
+        // per K chunk, the 16 diagonal elements: slot j's element is its
+        // accumulator value j % 4
+        for (int c = 0; c < JC; ++c) {
+          const float* pp = part + (rr * JC + c) * 64;
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) v += pp[4 * jj + (jj & 3)];
+        }
+      } else {
+        const float* pp = part + (rr * BB + bb) * JC;
+        for (int c = 0; c < JC; ++c) v += pp[c];
+      }
       if constexpr (PERROW) {
         uint16_t sb;
         int32_t zz;
@@ -532,12 +561,21 @@ hipError_t launch_t(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   int lgjc = 0;
   while ((tiles_per_wg << lgjc) < kItemsPerWave * kWaves && (2 << lgjc) <= J) ++lgjc;
   const int JC = 1 << lgjc;
-  int RT = kPartMax / (R * BB * JC);
+  // partial sums per tile: one float per (row, batch row, K chunk), or at
+  // batch 1 with one group per row 64 (the diagonal lanes' accumulators)
+  constexpr bool MD = BB == 1 && PERROW;
+  const size_t fixed = (size_t)J * U::QUADS * BB * 64 * sizeof(uint4) +
+                       (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) + 16;
+  const size_t per_tile = (size_t)R * BB * JC * sizeof(float) * (MD ? 64 : 1);
+  const size_t avail = device_lds_per_block() < kLdsBudget ? device_lds_per_block() : kLdsBudget;
+  if (fixed + per_tile > avail) return hipErrorNotSupported;
+  int RT = MD ? (int)((kPartMaxMD * sizeof(float) < avail - fixed ? kPartMaxMD * sizeof(float)
+                                                                   : avail - fixed) /
+                      per_tile)
+              : kPartMax / (R * BB * JC);
   if (RT > tiles_per_wg) RT = tiles_per_wg;
   if (RT < 1) return hipErrorNotSupported;
-  size_t lds = (size_t)J * U::QUADS * BB * 64 * sizeof(uint4) +
-               (size_t)kWaves * U::WORDS * 64 * sizeof(uint32_t) +
-               (size_t)RT * R * BB * JC * sizeof(float) + 16;
+  size_t lds = fixed + (size_t)RT * per_tile;
   if (lds > device_lds_per_block() || lds > kLdsBudget) return hipErrorNotSupported;
   // Occupancy bound: the work split gives every workgroup an equal share of
   // the rows and assumes one workgroup per CU.  A request above half of the

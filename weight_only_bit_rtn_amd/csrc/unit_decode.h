@@ -325,6 +325,23 @@ __device__ __forceinline__ bool make_pconsts(const HalfParams& hp, PConsts<BITS>
   return ok;
 }
 
+// make_pconsts for one wave-uniform zero point z shared by both halves (one
+// group per row), by scalar integer operations only, for the zero points of
+// every row whose range contains 0 (0 <= z < 2^(10 - PMAX)).  Returns false
+// for any other z: the caller then takes its exact per-code path (a
+// conversion here would move the constants into vector registers).
+template <int BITS>
+__device__ __forceinline__ bool row_pconsts(int32_t z, PConsts<BITS>& c) {
+  using U = Unit<BITS>;
+  const uint32_t z2 = ((uint32_t)z & 0xffffu) | ((uint32_t)z << 16);
+#pragma unroll
+  for (int p = 0; p <= U::PMAX; ++p) {
+    if (!U::uses(p)) continue;
+    c.hz[U::pidx(p)] = as_h2((uint32_t)(25 - p) * 0x04000400u + (z2 << p));
+  }
+  return (uint32_t)z < (1024u >> U::PMAX);
+}
+
 // q - z of both codes of slot s, exact: (2^(10 - p) + q) - (2^(10 - p) + z).
 template <int BITS>
 __device__ __forceinline__ h2_t qz_pair(const uint32_t (&w)[Unit<BITS>::WORDS], int s,
