@@ -64,7 +64,9 @@
  * device-side fault surfaces at the caller's next synchronization.  Inputs
  * must be finite.  Outputs must not alias inputs.  The library allocates no
  * memory and keeps no per-call state: calls on different streams may run
- * concurrently as long as their output buffers do not overlap.
+ * concurrently as long as their output buffers do not overlap.  (The one
+ * exception is lowbit_quantize_gptq_noalloc, whose workspace is a static
+ * device array of the library: see there.)
  */
 #ifndef LOWBIT_H
 #define LOWBIT_H
@@ -84,9 +86,11 @@ extern "C" {
 #define LOWBIT_ERR_SHAPE (-2)       /* K or group_size break the shape rules */
 #define LOWBIT_ERR_UNSUPPORTED (-3) /* bits not in {2, 3, 4, 8} */
 #define LOWBIT_ERR_HIP (-4)         /* the HIP runtime refused a launch or query */
+#define LOWBIT_ERR_SCRATCH (-5)     /* larger than lowbit_quantize_gptq_noalloc's static scratch */
 
 #define LOWBIT_QUANTIZE_MAX_K 131072
 #define LOWBIT_QGEMV_MAX_B 15
+#define LOWBIT_GPTQ_NOALLOC_MAX_BYTES 75497472 /* 72 MiB */
 
 /*
  * Quantize fp16 weights w[N][K] with min-max RTN (BladeLLM model
@@ -231,6 +235,30 @@ LOWBIT_API int lowbit_quantize_gptq_sym(const void* w_f16, int64_t N, int64_t K,
                                         uint32_t* packed_or_null, uint16_t* scales_f16,
                                         int32_t* zeros, void* workspace,
                                         int64_t workspace_bytes, void* hip_stream);
+
+/*
+ * lowbit_quantize_gptq without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same computation, arguments, layouts,
+ * shape rules and outputs as lowbit_quantize_gptq on the min-max grid; the
+ * fp64 workspace is instead a static device array inside the library, of
+ * LOWBIT_GPTQ_NOALLOC_MAX_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  A problem whose lowbit_gptq_workspace_bytes(N, K)
+ * exceeds it returns LOWBIT_ERR_SCRATCH before anything is enqueued (e.g.
+ * N = K = 2048 fits; N = 11008, K = 4096 does not).  The status word (0, or
+ * 1 when H was not positive definite) is written to *status_or_null (a
+ * 4-byte aligned device int32 owned by the caller; NULL: not reported).
+ * This entry point allocates nothing and calls no allocating routine.  All
+ * calls on one GPU share the array and each call overwrites what the
+ * previous one left there: calls that overlap on one GPU (different streams
+ * or host threads) race and must be serialized by the caller.
+ */
+LOWBIT_API int lowbit_quantize_gptq_noalloc(const void* w_f16, int64_t N, int64_t K,
+                                            const void* x_f16, int64_t n_samples, double damp,
+                                            int bits, int64_t group_size, uint8_t* codes_or_null,
+                                            uint32_t* packed_or_null, uint16_t* scales_f16,
+                                            int32_t* zeros, int32_t* status_or_null,
+                                            void* hip_stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 LOWBIT_API const char* lowbit_status_string(int status);

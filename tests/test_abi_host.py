@@ -32,7 +32,7 @@ def test_header_declares_the_abi():
     assert declared_entry_points() == sorted(
         ["lowbit_pack", "lowbit_pack_meta", "lowbit_qgemm", "lowbit_qgemm_meta", "lowbit_qgemv",
          "lowbit_qgemv_meta", "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym",
-         "lowbit_quantize_rtn",
+         "lowbit_quantize_gptq_noalloc", "lowbit_quantize_rtn",
          "lowbit_quantize_rtn_sym", "lowbit_gptq_workspace_bytes", "lowbit_status_string"])
 
 
@@ -53,10 +53,12 @@ def test_header_constants_match_binding(lw):
     assert int(consts["LOWBIT_ERR_HIP"]) == lw.LOWBIT_ERR_HIP
     assert int(consts["LOWBIT_QGEMV_MAX_B"]) == lw.QGEMV_MAX_B
     assert int(consts["LOWBIT_QUANTIZE_MAX_K"]) == lw.QUANTIZE_MAX_K
+    assert int(consts["LOWBIT_ERR_SCRATCH"]) == lw.LOWBIT_ERR_SCRATCH
+    assert int(consts["LOWBIT_GPTQ_NOALLOC_MAX_BYTES"]) == lw.GPTQ_NOALLOC_MAX_BYTES
 
 
 def test_status_strings(lw):
-    for st in (0, -1, -2, -3, -4, 17):
+    for st in (0, -1, -2, -3, -4, -5, 17):
         s = lw.status_string(st)
         assert isinstance(s, str) and s
     assert lw.status_string(0) == "ok"
@@ -143,6 +145,22 @@ HOST_VALIDATION_CASES = [
                                          None), "ARG"),
     (lambda lw: lw.quantize_gptq_sym_raw(None, 0, 128, None, 64, 0.01, 4, 0, None, None, None,
                                          None, None, 0, None), "OK"),
+    # the no-allocation error-feedback entry point: same checks, plus the
+    # static scratch bound (11008 x 4096 needs ~513 MB) and the status word
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 4, 128, P, 64, 0.01, 6, 0, P, P, P, P, None,
+                                             None), "UNSUPPORTED"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 4, 96, P, 64, 0.01, 4, 64, P, P, P, P, None,
+                                             None), "SHAPE"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 4, 128, P, 64, 0.0, 4, 0, P, P, P, P, None,
+                                             None), "ARG"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 4, 128, P, 64, 0.01, 4, 0, P, P, P, P, P + 2,
+                                             None), "ARG"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 4, 128, None, 64, 0.01, 4, 0, P, P, P, P, None,
+                                             None), "ARG"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(P, 11008, 4096, P, 64, 0.01, 2, 64, P, P, P, P, P,
+                                             None), "SCRATCH"),
+    (lambda lw: lw.quantize_gptq_noalloc_raw(None, 0, 128, None, 64, 0.01, 4, 0, None, None,
+                                             None, None, None, None), "OK"),
     # empty problems are valid and launch nothing
     (lambda lw: lw.quantize_rtn_raw(None, 0, 128, 4, 0, None, None, None, None, None), "OK"),
     (lambda lw: lw.qgemv_raw(None, 0, None, None, None, 8, 128, 4, 0, None, None), "OK"),
@@ -153,7 +171,7 @@ HOST_VALIDATION_CASES = [
 
 def expected_status(lw, status: str) -> int:
     return {"OK": lw.LOWBIT_OK, "ARG": lw.LOWBIT_ERR_ARG, "SHAPE": lw.LOWBIT_ERR_SHAPE,
-            "UNSUPPORTED": lw.LOWBIT_ERR_UNSUPPORTED}[status]
+            "UNSUPPORTED": lw.LOWBIT_ERR_UNSUPPORTED, "SCRATCH": lw.LOWBIT_ERR_SCRATCH}[status]
 
 
 @pytest.mark.parametrize("call,status", HOST_VALIDATION_CASES)
@@ -166,6 +184,13 @@ def test_binding_refuses_cpu_tensors(lw):
     w = torch.zeros(4, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         lw.quantize_rtn(w, 4, 0)
+
+
+def test_gptq_noalloc_scratch_bound(lw):
+    """The largest workspace the static scratch holds: the 2048 x 2048 layer
+    fits, the Llama-7B 11008 x 4096 layer does not."""
+    assert lw.gptq_workspace_bytes(2048, 2048) <= lw.GPTQ_NOALLOC_MAX_BYTES
+    assert lw.gptq_workspace_bytes(11008, 4096) > lw.GPTQ_NOALLOC_MAX_BYTES
 
 
 def test_gptq_workspace_size(lw):

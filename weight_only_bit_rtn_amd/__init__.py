@@ -30,12 +30,15 @@ LOWBIT_ERR_ARG = -1
 LOWBIT_ERR_SHAPE = -2
 LOWBIT_ERR_UNSUPPORTED = -3
 LOWBIT_ERR_HIP = -4
+LOWBIT_ERR_SCRATCH = -5
 QGEMV_MAX_B = 15
 QUANTIZE_MAX_K = 131072
+GPTQ_NOALLOC_MAX_BYTES = 72 << 20
 
 EXPORTED = ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv", "lowbit_qgemm",
             "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta", "lowbit_gptq_workspace_bytes",
-            "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym", "lowbit_status_string")
+            "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym", "lowbit_quantize_gptq_noalloc",
+            "lowbit_status_string")
 
 _lib = None
 
@@ -67,11 +70,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowbit_quantize_gptq.argtypes = [vp, i64, i64, vp, i64, ctypes.c_double, i32, i64, vp,
                                          vp, vp, vp, vp, i64, vp]
     lib.lowbit_quantize_gptq_sym.argtypes = lib.lowbit_quantize_gptq.argtypes
+    lib.lowbit_quantize_gptq_noalloc.argtypes = [vp, i64, i64, vp, i64, ctypes.c_double, i32,
+                                                 i64, vp, vp, vp, vp, vp, vp]
     lib.lowbit_qgemv_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     lib.lowbit_qgemm_meta.argtypes = [vp, i64, vp, vp, i64, i64, i32, i64, vp, vp]
     for name in ("lowbit_quantize_rtn", "lowbit_quantize_rtn_sym", "lowbit_pack", "lowbit_qgemv",
                  "lowbit_qgemm", "lowbit_pack_meta", "lowbit_qgemv_meta", "lowbit_qgemm_meta",
-                 "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym"):
+                 "lowbit_quantize_gptq", "lowbit_quantize_gptq_sym",
+                 "lowbit_quantize_gptq_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lowbit_status_string.argtypes = [ctypes.c_int]
     lib.lowbit_status_string.restype = ctypes.c_char_p
@@ -302,6 +308,16 @@ def quantize_gptq_sym_raw(w, N, K, x, n, damp, bits, group_size, codes, packed, 
     return load_library().lowbit_quantize_gptq_sym(w, N, K, x, n, float(damp), bits, group_size,
                                                    codes, packed, scales, zeros, workspace,
                                                    workspace_bytes, stream)
+
+
+def quantize_gptq_noalloc_raw(w, N, K, x, n, damp, bits, group_size, codes, packed, scales,
+                              zeros, status, stream) -> int:
+    """lowbit_quantize_gptq_noalloc: the min-max error-feedback quantizer in the
+    library's static device scratch (no workspace argument, nothing allocated);
+    `status` is a device int32 address or None."""
+    return load_library().lowbit_quantize_gptq_noalloc(w, N, K, x, n, float(damp), bits,
+                                                       group_size, codes, packed, scales, zeros,
+                                                       status, stream)
 
 
 def quantize_gptq(w, x_calib, bits: int, group_size: int, damp: float = 0.01,

@@ -61,6 +61,9 @@ hipError_t raise_lds_limit(const void* kernel, int bytes) {
 
 }  // namespace lowbit
 
+static_assert(LOWBIT_GPTQ_NOALLOC_MAX_BYTES == lowbit::kGptqScratchBytes,
+              "the header's scratch size and the library's must agree");
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -267,6 +270,32 @@ int lowbit_quantize_gptq_sym(const void* w_f16, int64_t N, int64_t K, const void
                       workspace_bytes, hip_stream);
 }
 
+int lowbit_quantize_gptq_noalloc(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
+                                 int64_t n_samples, double damp, int bits, int64_t group_size,
+                                 uint8_t* codes_or_null, uint32_t* packed_or_null,
+                                 uint16_t* scales_f16, int32_t* zeros, int32_t* status_or_null,
+                                 void* hip_stream) {
+  int rc = check_bits(bits);
+  if (rc != LOWBIT_OK) return rc;
+  rc = check_shape(N, K, bits, group_size);
+  if (rc != LOWBIT_OK) return rc;
+  if (K > LOWBIT_QUANTIZE_MAX_K || N > INT32_MAX) return LOWBIT_ERR_SHAPE;
+  if (!(damp > 0.0) || !(damp < 1e300) || n_samples <= 0) return LOWBIT_ERR_ARG;
+  if (N == 0) return LOWBIT_OK;
+  if (!w_f16 || !x_f16 || !scales_f16 || !zeros || (!codes_or_null && !packed_or_null))
+    return LOWBIT_ERR_ARG;
+  if (!aligned16(w_f16) || !aligned16(x_f16) || !aligned16(scales_f16) || !aligned16(zeros) ||
+      (codes_or_null && !aligned16(codes_or_null)) ||
+      (packed_or_null && !aligned16(packed_or_null)) ||
+      (status_or_null && (reinterpret_cast<uintptr_t>(status_or_null) & 3u) != 0))
+    return LOWBIT_ERR_ARG;
+  if (lowbit::gptq_workspace_bytes(N, K) > lowbit::kGptqScratchBytes) return LOWBIT_ERR_SCRATCH;
+  return hip_status(lowbit::launch_gptq_noalloc(
+      static_cast<const uint16_t*>(w_f16), N, K, static_cast<const uint16_t*>(x_f16), n_samples,
+      damp, bits, group_size, codes_or_null, packed_or_null, scales_f16, zeros, status_or_null,
+      static_cast<hipStream_t>(hip_stream)));
+}
+
 const char* lowbit_status_string(int status) {
   switch (status) {
     case LOWBIT_OK:
@@ -280,6 +309,9 @@ const char* lowbit_status_string(int status) {
       return "unsupported bit width (2, 3, 4 or 8)";
     case LOWBIT_ERR_HIP:
       return "HIP runtime error while launching";
+    case LOWBIT_ERR_SCRATCH:
+      return "problem larger than the static scratch of lowbit_quantize_gptq_noalloc "
+             "(LOWBIT_GPTQ_NOALLOC_MAX_BYTES of workspace)";
     default:
       return "unknown status";
   }

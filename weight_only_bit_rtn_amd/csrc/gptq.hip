@@ -35,6 +35,8 @@
 // (scales, zero points) is the RTN grid of the original weights
 // (min-max, or signed symmetric with codes from 1), written by the RTN
 // quantizer before step 4.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -356,6 +358,57 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
 }
 
 }  // namespace
+
+// The no-allocation entry point's workspace: a file-scope device array of
+// kGptqScratchBytes (each GPU the library runs on holds its own copy until the
+// process ends).  In host code `gptq_scratch` only names the symbol; its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is passed to kernels.
+namespace {
+
+__device__ __align__(256) unsigned char gptq_scratch[kGptqScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Copies the status word of a run into the caller's output.
+__global__ void copy_status_kernel(const int32_t* __restrict__ from, int32_t* __restrict__ to) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) to[0] = from[0];
+}
+
+}  // namespace
+
+hipError_t gptq_scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(gptq_scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_gptq_noalloc(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
+                               int64_t n_samples, double damp, int bits, int64_t group_size,
+                               uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
+                               int32_t* status_out, hipStream_t stream) {
+  void* ws = nullptr;
+  hipError_t e = gptq_scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  e = launch_gptq(w, N, K, x, n_samples, damp, bits, group_size, false, codes, packed, scales,
+                  zeros, ws, stream);
+  if (e != hipSuccess || status_out == nullptr) return e;
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream,
+                     static_cast<const int32_t*>(ws), status_out);
+  return hipGetLastError();
+}
 
 size_t gptq_workspace_bytes(int64_t N, int64_t K) {
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };

@@ -27,6 +27,16 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
                        uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
                        void* workspace, hipStream_t stream);
 
+// The same in the library's own static device scratch (kGptqScratchBytes per
+// device; the caller checks gptq_workspace_bytes(N, K) against it): no
+// allocation.  The run's status word is copied to *status_out when it is
+// non-null.  Calls that overlap on one device race on the scratch.
+constexpr size_t kGptqScratchBytes = (size_t)72 << 20;
+hipError_t launch_gptq_noalloc(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
+                               int64_t n_samples, double damp, int bits, int64_t group_size,
+                               uint8_t* codes, uint32_t* packed, uint16_t* scales, int32_t* zeros,
+                               int32_t* status_out, hipStream_t stream);
+
 // The products take the group parameters as separate scales and zeros, or
 // (meta = true) as compact words passed through `scales` (zeros unused).
 
