@@ -259,6 +259,44 @@ def test_products_wide_groups_ragged(lw, bits, N, K, g, kind):
     _check_product(lw, w, bits, g, [1, 4], "qgemv")
 
 
+# The small-batch matrix-core GEMV (grouped 2- and 4-bit codes, 8 to 15
+# activation rows): one to three 16-row tiles per CU (257 tiles: two on one
+# CU), activations staged in several rounds (K up to 8256 at 15 rows), a last
+# step running past the row end (units per row not a multiple of four), one,
+# two, three and four units per group, ragged tiles; compared on every output
+# with the oracle, and bit for bit with the compact group words.
+MMA_CASES = [(2, 4100, 8256, 64), (2, 4100, 4224, 128), (2, 33, 1344, 192), (4, 4100, 4128, 32),
+             (4, 4100, 2016, 96), (4, 700, 8192, 128), (4, 50, 4224, 64)]
+
+
+@pytest.mark.parametrize("bits,N,K,g", MMA_CASES)
+def test_qgemv_matrix_core_batches(lw, bits, N, K, g):
+    import torch
+    _say(f"[small-batch matrix-core] bits={bits} N={N} K={K} g={g}")
+    w = _weights("mixed", N, K, seed=N + 11 * K + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    p, s, z = _to_gpu(packed), _to_gpu(scales), _to_gpu(zeros)
+    meta = lw.pack_meta(s, z)
+    for B in (8, 9, 12, 15):
+        x = harness.synth.normal_f16(B, K, 1.0, seed=B + 29, stream=2)
+        xg = _to_gpu(x)
+        y = lw.qgemv(xg, p, s, z, K, bits, g)
+        ym = lw.qgemv_meta(xg, p, meta, K, bits, g)
+        torch.cuda.synchronize()
+        assert torch.equal(ym.view(torch.int16), y.view(torch.int16)), f"B={B} compact words"
+        y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g)
+        harness.assert_y_close(y.cpu().numpy(), y_ref, f"qgemv bits={bits} N={N} K={K} g={g} B={B}")
+
+
+# Layers of more than three 16-row tiles per CU (on 256 CUs) hand grouped
+# 2- and 4-bit products of 5 to 8 activation rows to the matrix-core GEMM.
+@pytest.mark.parametrize("bits,N,K,g", [(4, 12320, 1024, 128), (2, 12320, 1024, 64)])
+def test_qgemv_tall_layers(lw, bits, N, K, g):
+    _say(f"[tall layers] bits={bits} N={N} K={K} g={g}")
+    w = _weights("normal", N, K, seed=N + 7 * K + bits)
+    _check_product(lw, w, bits, g, [4, 5, 8], "qgemv")
+
+
 # At least five 16-row groups per workgroup (on 256 CUs), so a whole 512-k
 # step sits in one K part, and G a multiple of 8, with the group exactly a
 # step run's span: at batch tiles of 16 and 32 rows the matrix-core product

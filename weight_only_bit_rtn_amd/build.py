@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
-SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemv2.hip", "gemv3.hip", "gemv4.hip", "gemv8.hip", "gemm.hip", "gptq.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemv2.hip", "gemv3.hip", "gemv4.hip", "gemv8.hip", "gemv_mma.hip", "gemm.hip", "gptq.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -2,10 +2,13 @@
 //
 // Batches 1..8 run on the VALU kernel (gemv_kernel.h), in passes of four
 // rows when the activations of all rows do not fit the on-chip staging
-// budget.  From 9 rows on, and when even four rows do not fit, the product
-// goes to the matrix-core kernel (gemm.hip): at those batch sizes the
-// per-weight work is dominated by the batch-many multiply-adds, which the
-// fp16 MFMA units do for free while the VALU only decodes.
+// budget; grouped 2- and 4-bit codes take the small-batch matrix-core kernel
+// (gemv_mma.hip) where it was measured faster.  Otherwise, from 9 rows on,
+// and when even four rows do not fit, the product goes to the matrix-core
+// GEMM (gemm.hip): at those batch sizes the per-weight work is dominated by
+// the batch-many multiply-adds, which the fp16 MFMA units do for free while
+// the VALU only decodes.
+#include "common.h"
 #include "kernels.h"
 
 namespace lowbit {
@@ -45,6 +48,29 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
                         int bits, int64_t group_size, bool meta, uint16_t* y,
                         hipStream_t stream) {
+  // Grouped 2- and 4-bit codes may take the small-batch matrix-core form
+  // (gemv_mma.hip), which decodes each weight once for all activation rows
+  // but pays a longer start-up and stages the activations in rounds whose
+  // length shrinks with the tiles per workgroup.  Crossovers measured on
+  // MI355X (Llama-7B 2-bit g64 MLP layers, 4-bit g128 layers of 2048 x 2048
+  // and 28672 x 8192): it wins from 4 rows on when every CU holds one 16-row
+  // tile, from 8 rows on with two or three tiles per CU, from 5 rows on where
+  // the VALU kernel needs two passes, and against the GEMM from 9 rows on; on
+  // layers of more than three tiles per CU the GEMM wins from 5 rows on.
+  const bool grouped24 = group_size != 0 && (bits == 2 || bits == 4);
+  const int cus = device_cu_count();
+  const int64_t NT = (N + 15) / 16;
+  const int64_t tiles_per_cu = (NT + cus - 1) / cus;
+  const bool mma_suited = grouped24 && tiles_per_cu <= 3;
+  const bool mma_first =
+      mma_suited && (B > kGemvMaxValuBatch ||
+                     (NT >= cus && (B == kGemvMaxValuBatch || (B >= 4 && tiles_per_cu == 1))));
+  if (mma_first) {
+    const hipError_t e = launch_qgemv_mma(x, B, packed, scales, zeros, N, K, bits, group_size,
+                                          meta, y, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
+  if (grouped24 && !mma_suited && B > kGemvPassBatch) return hipErrorNotSupported;
   if (B > kGemvMaxValuBatch) return hipErrorNotSupported;
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
@@ -53,6 +79,10 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
   hipError_t e = launch_rows(x, b, packed, scales, zeros, n, k, G, gsz, gshift, bits, meta, y,
                              stream);
   if (e != hipErrorNotSupported || b <= kGemvPassBatch) return e;
+  if (mma_suited && NT >= cus) {
+    e = launch_qgemv_mma(x, B, packed, scales, zeros, N, K, bits, group_size, meta, y, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   // The activations of all rows do not fit on chip: passes of up to four rows
   // (the weights are read once per pass, which costs less than the matrix-core
   // path at these batch sizes).  Every pass has the on-chip needs of the first

@@ -40,6 +40,14 @@ hipError_t launch_gptq_noalloc(const uint16_t* w, int64_t N, int64_t K, const ui
 // The products take the group parameters as separate scales and zeros, or
 // (meta = true) as compact words passed through `scales` (zeros unused).
 
+// Small-batch product on the matrix cores (1..16 activation rows) for 2- and
+// 4-bit codes in groups of whole 16-byte units; hipErrorNotSupported for
+// other layouts and for shares of work it is not sized for.
+hipError_t launch_qgemv_mma(const uint16_t* x, int64_t B, const uint32_t* packed,
+                            const uint16_t* scales, const int32_t* zeros, int64_t N, int64_t K,
+                            int bits, int64_t group_size, bool meta, uint16_t* y,
+                            hipStream_t stream);
+
 // VALU dequant-GEMV; returns hipErrorNotSupported when x does not fit the
 // on-chip staging budget (the caller then uses the MFMA path).
 hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
