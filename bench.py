@@ -158,9 +158,10 @@ GPTQ_LAYERS = (("outlier_2048", 2048), ("llama7b_up_11008x4096", 4096))
 
 
 def gptq_flops(N: int, K: int, n: int) -> float:
-    """fp64 operations of one call: the Hessian (2 n K^2, full matrix), its
-    Cholesky factor (K^3 / 3) and the feedback product (N K^2)."""
-    return 2.0 * n * K * K + K ** 3 / 3.0 + float(N) * K * K
+    """fp64 operations of one call: the Hessian (n K^2: one triangle of the
+    symmetric matrix, 2 n per entry), its Cholesky factor (K^3 / 3) and the
+    feedback product (N K^2)."""
+    return float(n) * K * K + K ** 3 / 3.0 + float(N) * K * K
 
 
 def measure_gptq(lw, torch, stream: int) -> dict:

@@ -54,10 +54,13 @@ __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
 }
 
 // Step 1.  Workgroup (bi, bj) computes the 64 x 64 tile of H at rows
-// 64 bi.., columns 64 bj.. and stores it with both indices reversed.
+// 64 bi.., columns 64 bj.. and stores it with both indices reversed.  Only
+// tiles with bi <= bj are formed: H is symmetric and the later steps read the
+// lower triangle of reverse(H) alone (entries i >= j).
 // Thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty.., columns 4 tx...
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                       int K, double* __restrict__ Hrev) {
+  if (blockIdx.x > blockIdx.y) return;
   __shared__ double xi[kHChunk][64];
   __shared__ double xj[kHChunk][64];
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
