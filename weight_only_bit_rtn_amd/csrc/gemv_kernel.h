@@ -509,12 +509,20 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
       compute(cur, bufB);
       cur = nx;
     }
-    __syncthreads();
-
     // the round's outputs: sum the K chunks in order (one group per row: times
-    // the row's scale), coalesced stores
+    // the row's scale), coalesced stores.  The scale of each thread's first
+    // output is requested before the barrier, so that its latency overlaps
+    // the wait for the workgroup's last items.
     const int row0 = rt0 * R;
     const int nrows = min((rt0 + ntl) * R, N) - row0;
+    uint16_t sb_first = 0;
+    if constexpr (PERROW) {
+      if (tid < nrows * BB) {
+        int32_t zz;
+        RowParams<META>(scales, zeros, row0 + tid % nrows, G).at(0, sb_first, zz);
+      }
+    }
+    __syncthreads();
     for (int e = tid; e < nrows * BB; e += kThreads) {
       const int bb = e / nrows, rr = e - bb * nrows;
       float v = 0.0f;
@@ -531,9 +539,9 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(
         for (int c = 0; c < JC; ++c) v += pp[c];
       }
       if constexpr (PERROW) {
-        uint16_t sb;
+        uint16_t sb = sb_first;
         int32_t zz;
-        RowParams<META>(scales, zeros, row0 + rr, G).at(0, sb, zz);
+        if (e != tid) RowParams<META>(scales, zeros, row0 + rr, G).at(0, sb, zz);
         v *= h_bits_to_f32(sb);
       }
       y[(int64_t)bb * N + row0 + rr] = f32_to_h_bits(v);
