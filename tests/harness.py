@@ -103,17 +103,6 @@ def oracle_abs_y(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: n
     return oracle.matmul_f64(np.abs(x), np.abs(deq))
 
 
-def sample_rows(N: int, count: int = 768, seed: int = 0) -> np.ndarray:
-    """Evenly spread rows plus both ends and random picks (sorted, unique)."""
-    if N <= count:
-        return np.arange(N)
-    rng = np.random.default_rng(seed)
-    picks = np.concatenate([np.linspace(0, N - 1, count // 2).astype(np.int64),
-                            rng.choice(N, count // 2, replace=False),
-                            np.array([0, 1, N - 2, N - 1])])
-    return np.unique(picks)
-
-
 def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray, what: str,
                    abs_terms: np.ndarray | None = None, K: int = 0) -> None:
     """Per-element tolerance check.

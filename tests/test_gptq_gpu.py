@@ -7,7 +7,7 @@ equal) ways, so a code could differ only where a quotient falls within about
 1e-12 of a rounding midpoint, which seeded continuous inputs do not produce.
 Shapes cover K that is not a multiple of the 64-column block, ragged row
 tiles, every width, per-row and grouped grids (power-of-two and other group
-sizes), and one workload layer at full size (rows sampled for the oracle).
+sizes), and one workload layer at full size (every row through the oracle).
 """
 from __future__ import annotations
 
