@@ -44,7 +44,9 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kNB = 64;    // Cholesky panel width and GPTQ column block
+constexpr int kNB = 64;    // GPTQ column block
+constexpr int kCB = 32;    // Cholesky panel width (one lane per row of the diagonal block)
+static_assert(kCB <= 64, "the diagonal block is factored by one wave");
 constexpr int kRows = 64;  // weight rows per GPTQ workgroup
 constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
 constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
@@ -125,14 +127,14 @@ __global__ __launch_bounds__(1024) void damp_kernel(double* __restrict__ A, int 
 // its diagonal are never used).
 __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ A, int K, int kb,
                                                        int nb, int32_t* __restrict__ status) {
-  __shared__ double col[kNB];
+  __shared__ double col[kCB];
   const int r = threadIdx.x;
-  double a[kNB];
+  double a[kCB];
 #pragma unroll
-  for (int c = 0; c < kNB; ++c)
+  for (int c = 0; c < kCB; ++c)
     a[c] = (r < nb && c < nb) ? A[(int64_t)(kb + r) * K + kb + c] : (c == r ? 1.0 : 0.0);
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     if (c < nb) {
       double d = __shfl(a[c], c);
       if (!(d > 0.0)) {
@@ -145,14 +147,14 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ A, i
       col[r] = lrc;
       __syncthreads();
 #pragma unroll
-      for (int k = c + 1; k < kNB; ++k)
+      for (int k = c + 1; k < kCB; ++k)
         if (r >= k) a[k] -= lrc * col[k];
       __syncthreads();
     }
   }
   if (r < nb) {
 #pragma unroll
-    for (int c = 0; c < kNB; ++c)
+    for (int c = 0; c < kCB; ++c)
       if (c <= r) A[(int64_t)(kb + r) * K + kb + c] = a[c];
   }
 }
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ A, i
 // x L11^T = a (forward substitution) for the row's nb panel entries.
 __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A, int K, int kb,
                                                          int nb) {
-  __shared__ double l[kNB][kNB + 1];
+  __shared__ double l[kCB][kCB + 1];
   const int tid = threadIdx.x;
   for (int e = tid; e < nb * nb; e += 256) {
     const int r = e / nb, c = e % nb;
@@ -171,11 +173,11 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A,
   const int r = kb + nb + blockIdx.x * 256 + tid;
   if (r >= K) return;
   double* row = A + (int64_t)r * K + kb;
-  double v[kNB];
+  double v[kCB];
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) v[c] = c < nb ? row[c] : 0.0;
+  for (int c = 0; c < kCB; ++c) v[c] = c < nb ? row[c] : 0.0;
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) {
+  for (int c = 0; c < kCB; ++c) {
     if (c < nb) {
       // four partial sums: a quarter of the dependent chain
       double s4[4] = {v[c], 0.0, 0.0, 0.0};
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A,
     }
   }
 #pragma unroll
-  for (int c = 0; c < kNB; ++c)
+  for (int c = 0; c < kCB; ++c)
     if (c < nb) row[c] = v[c];
 }
 
@@ -196,20 +198,20 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
                                                           int nb) {
   const int ti = blockIdx.x, tj = blockIdx.y;
   if (tj > ti) return;
-  __shared__ double li[64][kNB + 1];
-  __shared__ double lj[64][kNB + 1];
+  __shared__ double li[64][kCB + 1];
+  __shared__ double lj[64][kCB + 1];
   const int s0 = kb + nb;
   const int i0 = s0 + 64 * ti, j0 = s0 + 64 * tj;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  for (int e = tid; e < 64 * kNB; e += 256) {
-    const int r = e / kNB, k = e % kNB;
+  for (int e = tid; e < 64 * kCB; e += 256) {
+    const int r = e / kCB, k = e % kCB;
     li[r][k] = (i0 + r < K && k < nb) ? A[(int64_t)(i0 + r) * K + kb + k] : 0.0;
     lj[r][k] = (j0 + r < K && k < nb) ? A[(int64_t)(j0 + r) * K + kb + k] : 0.0;
   }
   __syncthreads();
   double acc[4][4] = {};
 #pragma unroll 4
-  for (int k = 0; k < kNB; ++k) {
+  for (int k = 0; k < kCB; ++k) {
     double a[4], b[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -439,9 +441,9 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   hipLaunchKernelGGL(hessian_kernel, dim3(tiles, tiles), dim3(256), 0, stream, x, n_samples, k,
                      A);
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, A, k, damp, status);
-  for (int kb = 0; kb < k; kb += kNB) {
-    const int nb = k - kb < kNB ? k - kb : kNB;
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, stream, A, k, kb, nb, status);
+  for (int kb = 0; kb < k; kb += kCB) {
+    const int nb = k - kb < kCB ? k - kb : kCB;
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kCB), 0, stream, A, k, kb, nb, status);
     const int below = k - kb - nb;
     if (below > 0) {
       hipLaunchKernelGGL(chol_panel_kernel, dim3((below + 255) / 256), dim3(256), 0, stream, A,
