@@ -53,10 +53,11 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
   // but pays a longer start-up and stages the activations in rounds whose
   // length shrinks with the tiles per workgroup.  Crossovers measured on
   // MI355X (Llama-7B 2-bit g64 MLP layers, 4-bit g128 layers of 2048 x 2048
-  // and 28672 x 8192): it wins from 4 rows on when every CU holds one 16-row
-  // tile, from 8 rows on with two or three tiles per CU, from 5 rows on where
-  // the VALU kernel needs two passes, and against the GEMM from 9 rows on; on
-  // layers of more than three tiles per CU the GEMM wins from 5 rows on.
+  // and 28672 x 8192): on layers of at least one 16-row tile per CU it wins
+  // from 5 rows on with up to three tiles per CU and from 4 rows on with one;
+  // against the GEMM it wins from 9 rows on at any height up to three tiles
+  // per CU; on layers of more than three tiles per CU the GEMM wins from 5
+  // rows on.
   const bool grouped24 = group_size != 0 && (bits == 2 || bits == 4);
   const int cus = device_cu_count();
   const int64_t NT = (N + 15) / 16;
@@ -64,7 +65,7 @@ hipError_t launch_qgemv(const uint16_t* x, int64_t B, const uint32_t* packed,
   const bool mma_suited = grouped24 && tiles_per_cu <= 3;
   const bool mma_first =
       mma_suited && (B > kGemvMaxValuBatch ||
-                     (NT >= cus && (B == kGemvMaxValuBatch || (B >= 4 && tiles_per_cu == 1))));
+                     (NT >= cus && (B > kGemvPassBatch || (B == kGemvPassBatch && tiles_per_cu == 1))));
   if (mma_first) {
     const hipError_t e = launch_qgemv_mma(x, B, packed, scales, zeros, N, K, bits, group_size,
                                           meta, y, stream);

@@ -16,7 +16,8 @@
 // S_g, which depend on x alone and are formed while x is staged.  Nothing
 // depends on the zero point's size, so no exact slow path is needed.
 //
-// Layout on gfx950 (16 waves per workgroup, one workgroup per CU):
+// Layout on gfx950 (one workgroup of 16 waves per CU, or two of 8 waves up to
+// 8 activation rows):
 //  - the weight rows form tiles of 16 (the MFMA's 16 columns n); a K step of
 //    a tile is 4 consecutive 16-byte units of each row: lane (n, h) loads
 //    unit h of its row (the row's four lanes read 64 contiguous bytes), then
@@ -43,15 +44,23 @@ namespace lowbit {
 
 namespace {
 
-constexpr int kMWaves = 16;
-constexpr int kMThreads = kMWaves * kWave;
+// Workgroups of W waves, 16 / W of them per CU: one of 16 waves, or two of
+// 8 (each then stages its own rounds, so one computes while the other waits
+// for its weights; measured faster up to 8 activation rows)
+template <int W>
+constexpr int kWgPerCu = 16 / W;
 // K steps per wave and round: two (three would not fit the 128 registers of a
 // 16-wave workgroup with separate scale and zero arrays; the compact-word
 // variant takes the same share so that both sum in the same order)
 constexpr int kAMax = 2;
-constexpr size_t kXsBudget = 64 * 1024;     // LDS for one round of activations
+// LDS for one round of activations: 64 KB with one workgroup per CU, 56 KB
+// with two
+template <int W>
+constexpr size_t kXsBudget = W == 16 ? 64 * 1024 : 56 * 1024;
 constexpr size_t kLdsCap = 160 * 1024;      // gfx950 LDS per CU
-constexpr size_t kOneWgPerCu = kLdsCap / 2 + 1024;
+// an LDS request that leaves room for kWgPerCu workgroups per CU and no more
+template <int W>
+constexpr size_t kWgLds = kLdsCap / (kWgPerCu<W> + 1) + 1024;
 
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
@@ -98,8 +107,8 @@ __device__ __forceinline__ uint32_t small_quotient(uint32_t n, uint32_t recip) {
   return recip ? __umulhi(n, recip) : n;
 }
 
-template <int BITS, bool META, int A>
-__global__ __launch_bounds__(kMThreads) void qgemv_mma_kernel(
+template <int BITS, bool META, int A, int W>
+__global__ __launch_bounds__(W * 64, kWgPerCu<W>) void qgemv_mma_kernel(
     const uint16_t* __restrict__ x, int B, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
     uint16_t* __restrict__ y, int N, int K, int G, uint32_t upg_recip, uint32_t b_recip, int RK,
@@ -134,7 +143,7 @@ __global__ __launch_bounds__(kMThreads) void qgemv_mma_kernel(
 
   // this wave's (tile, step) pairs: the same indices every round
   const int total = ntiles * SR;
-  const int a = (total + kMWaves - 1) / kMWaves;  // <= A (host)
+  const int a = (total + W - 1) / W;  // <= A (host)
   const int i0 = wave * a;
   const int tile_first = i0 / SR;
 
@@ -367,13 +376,13 @@ __global__ __launch_bounds__(kMThreads) void qgemv_mma_kernel(
     *reinterpret_cast<f4_t*>(part + ((wave * A + j) * 16 + nl) * 16 + 4 * h) = acc[j];
   __syncthreads();
   // each output: the segments of its tile, in wave order
-  for (int e = tid; e < ntiles * 16 * B; e += kMThreads) {
+  for (int e = tid; e < ntiles * 16 * B; e += (W * kWave)) {
     const int tl = e / (16 * B);
     const int rest = e - tl * 16 * B;
     const int m = rest / 16, n = rest - m * 16;
     const int row = (t0 + tl) * 16 + n;
     float v = 0.0f;
-    for (int w = 0; w < kMWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const int wi0 = w * a;
       if (wi0 >= total) break;
       const int first = wi0 / SR;
@@ -385,24 +394,24 @@ __global__ __launch_bounds__(kMThreads) void qgemv_mma_kernel(
   }
 }
 
-template <int BITS, bool META, int A>
+template <int BITS, bool META, int A, int W>
 hipError_t launch_mma_t(const uint16_t* x, int B, const uint32_t* packed,
                         const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
                         uint32_t upg_recip, uint32_t b_recip, int RK, int nrounds, int nwg,
                         size_t lds, uint16_t* y, hipStream_t stream) {
-  const auto kern = qgemv_mma_kernel<BITS, META, A>;
+  const auto kern = qgemv_mma_kernel<BITS, META, A, W>;
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kern),
                                        (int)(device_lds_per_block() < kLdsCap
                                                  ? device_lds_per_block()
                                                  : kLdsCap));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(kMThreads), lds, stream, x, B, packed, scales, zeros,
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(W * kWave), lds, stream, x, B, packed, scales, zeros,
                      y, N, K, G, upg_recip, b_recip, RK, nrounds);
   return hipGetLastError();
 }
 
-template <int BITS, bool META>
-hipError_t launch_mma_bits(const uint16_t* x, int B, const uint32_t* packed,
+template <int BITS, bool META, int W>
+hipError_t launch_mma_w(const uint16_t* x, int B, const uint32_t* packed,
                            const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
                            int gsz, uint16_t* y, hipStream_t stream) {
   constexpr int U = MU<BITS>::CODES;
@@ -416,34 +425,43 @@ hipError_t launch_mma_bits(const uint16_t* x, int B, const uint32_t* packed,
   if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return hipErrorNotSupported;
   const int NT = (N + 15) / 16;
   const int cus = device_cu_count();
-  const int nwg = NT < cus ? NT : cus;
+  const int nwg = NT < kWgPerCu<W> * cus ? NT : kWgPerCu<W> * cus;
   const int tiles_per_wg = (NT + nwg - 1) / nwg;
   // units per round: all of the row if it fits, bounded by the activation
   // budget, by one staging pass of the workgroup, and by kAMax steps per wave
   int RK = (units_per_row + 3) / 4 * 4;
-  const int by_lds = (int)(kXsBudget / ((size_t)U * B * 2)) / 4 * 4;
-  const int by_threads = kMThreads / (B * (U / 32)) / 4 * 4;
-  const int by_steps = kMWaves * kAMax / tiles_per_wg * 4;
+  const int by_lds = (int)(kXsBudget<W> / ((size_t)U * B * 2)) / 4 * 4;
+  const int by_threads = W * kWave / (B * (U / 32)) / 4 * 4;
+  const int by_steps = W * kAMax / tiles_per_wg * 4;
   RK = RK < by_lds ? RK : by_lds;
   RK = RK < by_threads ? RK : by_threads;
   RK = RK < by_steps ? RK : by_steps;
   if (RK < 4) return hipErrorNotSupported;
   const int nrounds = (units_per_row + RK - 1) / RK;
   // K steps per wave and round in the workgroups with the most tiles
-  const int steps = (tiles_per_wg * (RK / 4) + kMWaves - 1) / kMWaves;
-  size_t lds = (size_t)RK * U * B * 2 + (size_t)RK * 16 * 4 + (size_t)kMWaves * steps * 256 * 4;
-  if (lds > device_lds_per_block() || lds > kLdsCap) return hipErrorNotSupported;
-  if (lds < kOneWgPerCu && kOneWgPerCu <= device_lds_per_block()) lds = kOneWgPerCu;
+  const int steps = (tiles_per_wg * (RK / 4) + W - 1) / W;
+  size_t lds = (size_t)RK * U * B * 2 + (size_t)RK * 16 * 4 + (size_t)W * steps * 256 * 4;
+  if (lds > device_lds_per_block() || lds > kLdsCap / kWgPerCu<W>) return hipErrorNotSupported;
+  if (lds < kWgLds<W> && kWgLds<W> <= device_lds_per_block()) lds = kWgLds<W>;
   switch (steps) {
     case 1:
-      return launch_mma_t<BITS, META, 1>(x, B, packed, scales, zeros, N, K, G, upg_recip, b_recip,
+      return launch_mma_t<BITS, META, 1, W>(x, B, packed, scales, zeros, N, K, G, upg_recip, b_recip,
                                          RK, nrounds, nwg, lds, y, stream);
     case 2:
-      return launch_mma_t<BITS, META, 2>(x, B, packed, scales, zeros, N, K, G, upg_recip, b_recip,
+      return launch_mma_t<BITS, META, 2, W>(x, B, packed, scales, zeros, N, K, G, upg_recip, b_recip,
                                          RK, nrounds, nwg, lds, y, stream);
     default:
       return hipErrorNotSupported;
   }
+}
+
+// Up to 8 activation rows: two 8-wave workgroups per CU; above: one of 16.
+template <int BITS, bool META>
+hipError_t launch_mma_bits(const uint16_t* x, int B, const uint32_t* packed,
+                           const uint16_t* scales, const int32_t* zeros, int N, int K, int G,
+                           int gsz, uint16_t* y, hipStream_t stream) {
+  return B <= 8 ? launch_mma_w<BITS, META, 8>(x, B, packed, scales, zeros, N, K, G, gsz, y, stream)
+                : launch_mma_w<BITS, META, 16>(x, B, packed, scales, zeros, N, K, G, gsz, y, stream);
 }
 
 }  // namespace
