@@ -437,6 +437,18 @@ hipError_t launch_mma_w(const uint16_t* x, int B, const uint32_t* packed,
   RK = RK < by_threads ? RK : by_threads;
   RK = RK < by_steps ? RK : by_steps;
   if (RK < 4) return hipErrorNotSupported;
+  // With several rounds, a round's (tile, step) pairs are dealt to the waves
+  // in equal shares of a = ceil(pairs / W): prefer the longest round whose
+  // pairs fill every wave's share (e.g. 8 steps rather than 10 over 8 waves,
+  // where 10 would leave three waves idle).
+  if (RK < units_per_row) {
+    for (int rk = RK; rk >= 4; rk -= 4) {
+      if ((tiles_per_wg * (rk / 4)) % W == 0) {
+        RK = rk;
+        break;
+      }
+    }
+  }
   const int nrounds = (units_per_row + RK - 1) / RK;
   // K steps per wave and round in the workgroups with the most tiles
   const int steps = (tiles_per_wg * (RK / 4) + W - 1) / W;
