@@ -244,6 +244,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
   __shared__ double dsm[kChunk][kRows];     // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][kRows];         // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 1];       // R[jb + a][jb + c], the block's own rows
+  __shared__ double rdi[kNB];               // 1 / R[jb + a][jb + a]
   __shared__ uint16_t ws[kRows][kNB + 2];   // the block's original weights
   __shared__ uint32_t qs[kRows][kNB / 4];    // the block's codes, stored together
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -313,6 +314,9 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
     }
+    // the reciprocals of the block's diagonal, so the column walk's chain
+    // holds one division (the code decision) instead of two
+    for (int a = tid; a < kNB; a += 256) rdi[a] = a < nb ? 1.0 / Rat(jb + a, jb + a) : 1.0;
     for (int e = tid; e < kRows * kNB; e += 256) {
       const int rr = e / kNB, c = e % kNB;
       ws[rr][c] = (r0 + rr < N && c < nb) ? w[(int64_t)(r0 + rr) * K + jb + c] : (uint16_t)0;
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           const double s = first ? s0 : s1;
           const int64_t z = first ? z0 : z1;
           const double wv = h_bits_to_f64(ws[lane][j]);
-          const double t = wv + cb[j] / rb[j][j];
+          const double t = wv + cb[j] * rdi[j];
           int64_t q = (int64_t)__builtin_rint(t / s) + z;
           q = q < qlo ? qlo : (q > M ? M : q);
           // the dequantized weight (q - z) * s, exact in fp64
