@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
   __shared__ double dsm[kChunk][kRows];     // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][kRows];         // sum_{i < j} d_i R_ij of each (column, row)
-  __shared__ double rb[kNB][kNB + 1];       // R[jb + a][jb + c], the block's own rows
+  __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
   __shared__ double rdi[kNB];               // 1 / R[jb + a][jb + a]
   __shared__ uint16_t ws[kRows][kNB + 2];   // the block's original weights
   __shared__ uint32_t qs[kRows][kNB / 4];    // the block's codes, stored together
@@ -352,7 +352,23 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
           if (valid) DT[(int64_t)col * N + row] = d;
 #pragma unroll
-          for (int j2 = j + 1; j2 < kNB; ++j2) cb[j2] = __builtin_fma(d, rb[j][j2], cb[j2]);
+          // row j of the block's factor in 16-byte reads, four entries at a
+          // time, issued before their multiply-adds
+          for (int j2b = (j + 1) & ~1; j2b < kNB; j2b += 4) {
+            double r8[4];
+#pragma unroll
+            for (int t = 0; t < 4; t += 2) {
+              if (j2b + t < kNB) {
+                const double2 v = *reinterpret_cast<const double2*>(&rb[j][j2b + t]);
+                r8[t] = v.x, r8[t + 1] = v.y;
+              }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int j2 = j2b + t;
+              if (j2 > j && j2 < kNB) cb[j2] = __builtin_fma(d, r8[t], cb[j2]);
+            }
+          }
         }
       }
     }
