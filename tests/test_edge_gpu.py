@@ -259,12 +259,14 @@ def test_products_wide_groups_ragged(lw, bits, N, K, g, kind):
     _check_product(lw, w, bits, g, [1, 4], "qgemv")
 
 
-# The small-batch matrix-core GEMV (grouped 2- and 4-bit codes, 8 to 15
-# activation rows): one to three 16-row tiles per CU (257 tiles: two on one
-# CU), activations staged in several rounds (K up to 8256 at 15 rows), a last
-# step running past the row end (units per row not a multiple of four), one,
-# two, three and four units per group, ragged tiles; compared on every output
-# with the oracle, and bit for bit with the compact group words.
+# The small-batch matrix-core GEMV (grouped 2- and 4-bit codes; 5 to 8
+# activation rows on two 8-wave workgroups per CU, 9 to 15 on one of 16
+# waves): one to three 16-row tiles per CU (257 tiles: two on one CU),
+# activations staged in several rounds (K up to 8256 at 15 rows) whose length
+# is cut to fill every wave's share (5, 6 and 7 rows), a last step running
+# past the row end (units per row not a multiple of four), one, two, three
+# and four units per group, ragged tiles; compared on every output with the
+# oracle, and bit for bit with the compact group words.
 MMA_CASES = [(2, 4100, 8256, 64), (2, 4100, 4224, 128), (2, 33, 1344, 192), (4, 4100, 4128, 32),
              (4, 4100, 2016, 96), (4, 700, 8192, 128), (4, 50, 4224, 64)]
 
@@ -277,7 +279,7 @@ def test_qgemv_matrix_core_batches(lw, bits, N, K, g):
     codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
     p, s, z = _to_gpu(packed), _to_gpu(scales), _to_gpu(zeros)
     meta = lw.pack_meta(s, z)
-    for B in (8, 9, 12, 15):
+    for B in (5, 6, 7, 8, 9, 12, 15):
         x = harness.synth.normal_f16(B, K, 1.0, seed=B + 29, stream=2)
         xg = _to_gpu(x)
         y = lw.qgemv(xg, p, s, z, K, bits, g)
