@@ -20,9 +20,10 @@
 // L[K-1-i][K-1-j].
 //
 // Steps, all in fp64 on the caller's stream, in the caller's workspace:
-//  1. hessian_kernel: reverse(H) = (2/n) X^T X with both indices reversed;
+//  1. hessian_kernel: reverse(H) = (2/n) X^T X with both indices reversed
+//     (the lower triangle, which is all the later steps read);
 //  2. damp_kernel: damp * mean(diag) added to the diagonal; status cleared;
-//  3. right-looking blocked Cholesky of reverse(H) in place, 64 columns per
+//  3. right-looking blocked Cholesky of reverse(H) in place, 32 columns per
 //     panel: diagonal block in one workgroup (chol_diag_kernel), the panel
 //     below by row-wise substitution (chol_panel_kernel), the trailing lower
 //     triangle by 64x64 tiles (chol_update_kernel);
