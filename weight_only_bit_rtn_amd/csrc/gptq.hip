@@ -48,7 +48,7 @@ namespace {
 constexpr int kNB = 64;    // GPTQ column block
 constexpr int kCB = 32;    // Cholesky panel width (one lane per row of the diagonal block)
 static_assert(kCB <= 64, "the diagonal block is factored by one wave");
-constexpr int kRows = 64;  // weight rows per GPTQ workgroup
+constexpr int kRows = 64;  // weight rows per GPTQ workgroup (32 on shorter layers)
 constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
 constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
 
@@ -233,43 +233,52 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
     }
 }
 
-// Step 4.  Workgroup b owns rows r0 = 64 b .. r0 + 63 (lane = row).  DT is the
-// residual matrix transposed, DT[i][n] = d_i of row n, so that a wave's
-// loads of one column are contiguous.
+// Step 4.  Workgroup b owns rows r0 = RW b .. r0 + RW - 1 (lane = row; RW is
+// 32 when workgroups of 32 rows all fit on the CUs at once, else 64).
+// DT is the residual matrix transposed, DT[i][n] = d_i of row n, so that a
+// wave's loads of one column are contiguous.
+template <int RW>
 __global__ __launch_bounds__(256) void gptq_rows_kernel(
     const uint16_t* __restrict__ w, int N, int K, const double* __restrict__ L,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int G, int gsz,
     int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
     uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
-  __shared__ double dsm[kChunk][kRows];     // DT[i0 + ii][r0 + lane], their residuals
-  __shared__ double cs[kNB][kRows];         // sum_{i < j} d_i R_ij of each (column, row)
+  static_assert(RW % 16 == 0 && RW <= 64, "16-row product tiles, one lane per row");
+  constexpr int RT = RW / 16;                // product rows per thread
+  __shared__ double dsm[kChunk][RW];        // DT[i0 + ii][r0 + lane], their residuals
+  __shared__ double cs[kNB][RW];            // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
   __shared__ double rdi[kNB];               // 1 / R[jb + a][jb + a]
-  __shared__ uint16_t ws[kRows][kNB + 2];   // the block's original weights
-  __shared__ uint32_t qs[kRows][kNB / 4];    // the block's codes, stored together
+  __shared__ uint16_t ws[RW][kNB + 2];      // the block's original weights
+  __shared__ uint32_t qs[RW][kNB / 4];       // the block's codes, stored together
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r0 = blockIdx.x * kRows;
+  const int r0 = blockIdx.x * RW;
   const int row = r0 + lane;
-  const bool valid = row < N;
+  const bool valid = lane < RW && row < N;
+  const int lr = lane < RW ? lane : RW - 1;  // LDS row of the lane (lanes past RW idle)
   // R_ij = L[K-1-i][K-1-j]
   auto Rat = [&](int i, int j) { return L[(int64_t)(K - 1 - i) * K + (K - 1 - j)]; };
 
   for (int jb = 0; jb < K; jb += kNB) {
     const int nb = min(kNB, K - jb);
     // contribution of the columns before the block: thread (ty, tx) sums
-    // rows 4 ty .. 4 ty + 3 and block columns 4 tx .. 4 tx + 3
+    // rows RT ty .. RT ty + RT - 1 and block columns 4 tx .. 4 tx + 3
     const int ty = tid >> 4, tx = tid & 15;
-    double acc[4][4] = {};
+    double acc[RT][4] = {};
     // Chunks of 64 earlier columns: R rows and residuals staged in LDS, the
     // next chunk's loads issued (into registers) before this chunk's products.
     const int nchunks = jb / kChunk;
-    double pr[16], pd[16];
+    double pr[16], pd[RW / 4];
     auto fetch = [&](int i0) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
         pr[k] = c < nb ? Rat(i0 + ii, jb + c) : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < RW / 4; ++k) {
+        const int e = tid + 256 * k, ii = e / RW, c = e % RW;
         pd[k] = r0 + c < N ? DT[(int64_t)(i0 + ii) * N + r0 + c] : 0.0;
       }
     };
@@ -280,37 +289,39 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       for (int k = 0; k < 16; ++k) {
         const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
         rs[ii][c] = pr[k];
+      }
+#pragma unroll
+      for (int k = 0; k < RW / 4; ++k) {
+        const int e = tid + 256 * k, ii = e / RW, c = e % RW;
         dsm[ii][c] = pd[k];
       }
       __syncthreads();
       if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
       // operands of step ii + 1 are read while step ii multiplies
-      double a[2][4], b[2][4];
+      double a[2][RT], b[2][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[0][u] = dsm[0][4 * ty + u];
-        b[0][u] = rs[0][4 * tx + u];
-      }
+      for (int u = 0; u < RT; ++u) a[0][u] = dsm[0][RT * ty + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[0][u] = rs[0][4 * tx + u];
 #pragma unroll
       for (int ii = 0; ii < kChunk; ++ii) {
         const int cur = ii & 1, nxt = cur ^ 1;
         if (ii + 1 < kChunk) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            a[nxt][u] = dsm[ii + 1][4 * ty + u];
-            b[nxt][u] = rs[ii + 1][4 * tx + u];
-          }
+          for (int u = 0; u < RT; ++u) a[nxt][u] = dsm[ii + 1][RT * ty + u];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) b[nxt][u] = rs[ii + 1][4 * tx + u];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < RT; ++u)
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[cur][u], b[cur][v], acc[u][v]);
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < RT; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) cs[4 * tx + v][4 * ty + u] = acc[u][v];
+      for (int v = 0; v < 4; ++v) cs[4 * tx + v][RT * ty + u] = acc[u][v];
     for (int e = tid; e < kNB * kNB; e += 256) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     // the reciprocals of the block's diagonal, so the column walk's chain
     // holds one division (the code decision) instead of two
     for (int a = tid; a < kNB; a += 256) rdi[a] = a < nb ? 1.0 / Rat(jb + a, jb + a) : 1.0;
-    for (int e = tid; e < kRows * kNB; e += 256) {
+    for (int e = tid; e < RW * kNB; e += 256) {
       const int rr = e / kNB, c = e % kNB;
       ws[rr][c] = (r0 + rr < N && c < nb) ? w[(int64_t)(r0 + rr) * K + jb + c] : (uint16_t)0;
     }
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       const int64_t z1 = valid ? zeros[(int64_t)row * G + g1] : 0;
       double cb[kNB];
 #pragma unroll
-      for (int j = 0; j < kNB; ++j) cb[j] = cs[j][lane];
+      for (int j = 0; j < kNB; ++j) cb[j] = cs[j][lr];
 #pragma unroll
       for (int j = 0; j < kNB; ++j) {
         if (j < nb) {
@@ -343,18 +354,18 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
           const bool first = col / gsz == g0;
           const double s = first ? s0 : s1;
           const int64_t z = first ? z0 : z1;
-          const double wv = h_bits_to_f64(ws[lane][j]);
+          const double wv = h_bits_to_f64(ws[lr][j]);
           const double t = wv + cb[j] * rdi[j];
           int64_t q = (int64_t)__builtin_rint(t / s) + z;
           q = q < qlo ? qlo : (q > M ? M : q);
           // the dequantized weight (q - z) * s, exact in fp64
           const double deq = (double)(q - z) * s;
           const double d = wv - deq;
-          reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
+          if (lane < RW) reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
           if (valid) DT[(int64_t)col * N + row] = d;
-#pragma unroll
           // row j of the block's factor in 16-byte reads, four entries at a
           // time, issued before their multiply-adds
+#pragma unroll
           for (int j2b = (j + 1) & ~1; j2b < kNB; j2b += 4) {
             double r8[4];
 #pragma unroll
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     }
     __syncthreads();
     // the block's codes, four per store (K is a multiple of 32, jb of 64)
-    for (int e = tid; e < kRows * (kNB / 4); e += 256) {
+    for (int e = tid; e < RW * (kNB / 4); e += 256) {
       const int rr = e / (kNB / 4), c4 = e % (kNB / 4);
       if (r0 + rr < N && 4 * c4 < nb)
         *reinterpret_cast<uint32_t*>(codes + (int64_t)(r0 + rr) * K + jb + 4 * c4) = qs[rr][c4];
@@ -475,8 +486,17 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   }
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
-  hipLaunchKernelGGL(gptq_rows_kernel, dim3((n + kRows - 1) / kRows), dim3(256), 0, stream, w, n,
-                     k, A, scales, zeros, G, gsz, (1 << bits) - 1, sym ? 1 : 0, DT, out_codes);
+  // Rows per workgroup: 32 when those workgroups all run at once (one per
+  // CU), so that short layers spread over more CUs (the product part halves;
+  // the column walk does not change); else 64 (48 measured no faster on the
+  // 11008-row layer than 64).
+  const int qmax = (1 << bits) - 1, qlo = sym ? 1 : 0;
+  if ((n + 31) / 32 <= device_cu_count())
+    hipLaunchKernelGGL(gptq_rows_kernel<32>, dim3((n + 31) / 32), dim3(256), 0, stream, w, n, k, A,
+                       scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
+  else
+    hipLaunchKernelGGL(gptq_rows_kernel<kRows>, dim3((n + kRows - 1) / kRows), dim3(256), 0,
+                       stream, w, n, k, A, scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (packed) return launch_pack(out_codes, N, K, bits, packed, stream);
