@@ -108,6 +108,9 @@ HOST_VALIDATION_CASES = [
     (lambda lw: lw.qgemv_raw(P, 1, None, P, P, 4, 128, 4, 0, P, None), "ARG"),
     (lambda lw: lw.qgemm_raw(P, 1, P, P, P, 4, 128, 4, 0, MIS, None), "ARG"),
     (lambda lw: lw.qgemm_raw(MIS, 1, P, P, P, 4, 128, 4, 0, P, None), "ARG"),
+    # activations off a 16-byte boundary, at a batch the matrix-core GEMV takes
+    (lambda lw: lw.qgemv_raw(MIS, 12, P, P, P, 4100, 2048, 2, 64, P, None), "ARG"),
+    (lambda lw: lw.qgemv_meta_raw(MIS, 12, P, P, 4100, 2048, 2, 64, P, None), "ARG"),
     # compact metadata entry points
     (lambda lw: lw.pack_meta_raw(P, P, -1, 4, P, None, None), "ARG"),
     (lambda lw: lw.pack_meta_raw(None, P, 4, 4, P, None, None), "ARG"),

@@ -424,3 +424,4 @@ def test_calls_follow_the_callers_stream(lw):
     y_host = harness.oracle_y(x.cpu().numpy(), ref["packed"].cpu().numpy().view(np.uint32),
                               ref["scales"].cpu().numpy(), ref["zeros"].cpu().numpy(), K, bits, g)
     harness.assert_y_close(y2.cpu().numpy(), y_host, "qgemm on a side stream")
+
