@@ -193,12 +193,16 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A,
 }
 
 // Step 3c: trailing lower triangle from s0 = kb + nb on: A[i][j] -= sum_k
-// L[i][kb + k] L[j][kb + k], in 64 x 64 tiles (ti >= tj; the grid is square
-// and the upper tiles return at once).
+// L[i][kb + k] L[j][kb + k], in 64 x 64 tiles (ti >= tj), one workgroup per
+// tile of the lower triangle.
 __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A, int K, int kb,
                                                           int nb) {
-  const int ti = blockIdx.x, tj = blockIdx.y;
-  if (tj > ti) return;
+  // workgroup p takes tile (ti, tj) of the lower triangle, p = ti (ti + 1) / 2 + tj
+  const int p = (int)blockIdx.x;
+  int ti = (int)((__builtin_sqrtf(8.0f * (float)p + 1.0f) - 1.0f) * 0.5f);
+  while ((ti + 1) * (ti + 2) / 2 <= p) ++ti;
+  while (ti * (ti + 1) / 2 > p) --ti;
+  const int tj = p - ti * (ti + 1) / 2;
   __shared__ double li[64][kCB + 1];
   __shared__ double lj[64][kCB + 1];
   const int s0 = kb + nb;
@@ -481,7 +485,8 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
       hipLaunchKernelGGL(chol_panel_kernel, dim3((below + 255) / 256), dim3(256), 0, stream, A,
                          k, kb, nb);
       const int t = (below + 63) / 64;
-      hipLaunchKernelGGL(chol_update_kernel, dim3(t, t), dim3(256), 0, stream, A, k, kb, nb);
+      hipLaunchKernelGGL(chol_update_kernel, dim3(t * (t + 1) / 2), dim3(256), 0, stream, A, k, kb,
+                         nb);
     }
   }
   const int gsz = (int)(group_size == 0 ? K : group_size);
