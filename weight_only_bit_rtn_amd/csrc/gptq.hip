@@ -52,6 +52,8 @@ constexpr int kRows = 64;  // weight rows per GPTQ workgroup (32 on shorter laye
 constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
 constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
   return (double)__builtin_bit_cast(_Float16, b);
 }
@@ -60,15 +62,27 @@ __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
 // 64 bi.., columns 64 bj.. and stores it with both indices reversed.  Only
 // tiles with bi <= bj are formed: H is symmetric and the later steps read the
 // lower triangle of reverse(H) alone (entries i >= j).
-// Thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty.., columns 4 tx...
+// The products run on the fp64 matrix cores (v_mfma_f64_16x16x4f64,
+// D = A B + D with A 16 x 4, B 4 x 16): wave w owns the 32 x 32 quarter
+// (w / 2, w % 2) as 2 x 2 tiles; lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] (calibration row l / 16 of the 4-row step) and holds
+// D[l / 16 + 4 v][l % 16] in element v.  Operands come from the staged rows
+// in LDS, one read per lane and tile edge per 4 rows (eight times fewer LDS
+// reads per multiply-add than 4 x 4 register tiles on the vector units).
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                       int K, double* __restrict__ Hrev) {
   if (blockIdx.x > blockIdx.y) return;
   __shared__ double xi[kHChunk][64];
   __shared__ double xj[kHChunk][64];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-  double acc[4][4] = {};
+  const int ml = lane & 15, kl = lane >> 4;
+  const int mb = (wave >> 1) * 32, nbw = (wave & 1) * 32;
+  f64x4_t acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4_t{0.0, 0.0, 0.0, 0.0};
   for (int64_t t0 = 0; t0 < n; t0 += kHChunk) {
     for (int e = tid; e < kHChunk * 64; e += 256) {
       const int tt = e >> 6, c = e & 63;
@@ -77,29 +91,28 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
       xj[tt][c] = (t < n && j0 + c < K) ? h_bits_to_f64(x[t * K + j0 + c]) : 0.0;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int tt = 0; tt < kHChunk; ++tt) {
-      double a[4], b[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = xi[tt][4 * ty + u];
-        b[u] = xj[tt][4 * tx + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+    for (int kk = 0; kk < kHChunk / 4; ++kk) {
+      const int tt = 4 * kk + kl;
+      const double a0 = xi[tt][mb + ml], a1 = xi[tt][mb + 16 + ml];
+      const double b0 = xj[tt][nbw + ml], b1 = xj[tt][nbw + 16 + ml];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
     __syncthreads();
   }
   const double f = 2.0 / (double)n;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = i0 + 4 * ty + u, j = j0 + 4 * tx + v;
-      if (i < K && j < K) Hrev[(int64_t)(K - 1 - i) * K + (K - 1 - j)] = f * acc[u][v];
-    }
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + mb + 16 * u + kl + 4 * e, j = j0 + nbw + 16 * v + ml;
+        if (i < K && j < K) Hrev[(int64_t)(K - 1 - i) * K + (K - 1 - j)] = f * acc[u][v][e];
+      }
 }
 
 // Step 2 (one workgroup): diag += damp * trace / K; the status word is cleared.
