@@ -261,8 +261,8 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
     uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
-  static_assert(RW % 16 == 0 && RW <= 64, "16-row product tiles, one lane per row");
-  constexpr int RT = RW / 16;                // product rows per thread
+  static_assert(RW == 32 || RW == 64, "16-row product tiles, one lane per row");
+  constexpr int TU = RW / 32;                // 16-row product tiles per wave
   __shared__ double dsm[kChunk][RW];        // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][RW];            // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
@@ -270,6 +270,8 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
   __shared__ uint16_t ws[RW][kNB + 2];      // the block's original weights
   __shared__ uint32_t qs[RW][kNB / 4];       // the block's codes, stored together
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ml = lane & 15, kl = lane >> 4;
+  const int mb = (wave >> 1) * 16 * TU, nbw = (wave & 1) * 32;
   const int r0 = blockIdx.x * RW;
   const int row = r0 + lane;
   const bool valid = lane < RW && row < N;
@@ -279,10 +281,14 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
 
   for (int jb = 0; jb < K; jb += kNB) {
     const int nb = min(kNB, K - jb);
-    // contribution of the columns before the block: thread (ty, tx) sums
-    // rows RT ty .. RT ty + RT - 1 and block columns 4 tx .. 4 tx + 3
-    const int ty = tid >> 4, tx = tid & 15;
-    double acc[RT][4] = {};
+    // contribution of the columns before the block, on the fp64 matrix
+    // cores: wave w sums rows mb .. mb + 16 TU - 1 and block columns
+    // nbw .. nbw + 31 as TU x 2 tiles of 16 x 16 (lane layout as in step 1)
+    f64x4_t acc[TU][2];
+#pragma unroll
+    for (int u = 0; u < TU; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) acc[u][v] = f64x4_t{0.0, 0.0, 0.0, 0.0};
     // Chunks of 64 earlier columns: R rows and residuals staged in LDS, the
     // next chunk's loads issued (into registers) before this chunk's products.
     const int nchunks = jb / kChunk;
@@ -314,31 +320,27 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
       }
       __syncthreads();
       if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
-      // operands of step ii + 1 are read while step ii multiplies
-      double a[2][RT], b[2][4];
 #pragma unroll
-      for (int u = 0; u < RT; ++u) a[0][u] = dsm[0][RT * ty + u];
+      for (int kk = 0; kk < kChunk / 4; ++kk) {
+        const int ii = 4 * kk + kl;
+        double a[TU], b[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) b[0][u] = rs[0][4 * tx + u];
+        for (int u = 0; u < TU; ++u) a[u] = dsm[ii][mb + 16 * u + ml];
 #pragma unroll
-      for (int ii = 0; ii < kChunk; ++ii) {
-        const int cur = ii & 1, nxt = cur ^ 1;
-        if (ii + 1 < kChunk) {
+        for (int v = 0; v < 2; ++v) b[v] = rs[ii][nbw + 16 * v + ml];
 #pragma unroll
-          for (int u = 0; u < RT; ++u) a[nxt][u] = dsm[ii + 1][RT * ty + u];
+        for (int u = 0; u < TU; ++u)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) b[nxt][u] = rs[ii + 1][4 * tx + u];
-        }
-#pragma unroll
-        for (int u = 0; u < RT; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[cur][u], b[cur][v], acc[u][v]);
+          for (int v = 0; v < 2; ++v)
+            acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[u], b[v], acc[u][v], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < RT; ++u)
+    for (int u = 0; u < TU; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) cs[4 * tx + v][RT * ty + u] = acc[u][v];
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + 16 * u + kl + 4 * e] = acc[u][v][e];
     for (int e = tid; e < kNB * kNB; e += 256) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
