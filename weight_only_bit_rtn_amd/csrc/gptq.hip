@@ -29,8 +29,9 @@
 //     triangle by 64x64 tiles (chol_update_kernel);
 //  4. gptq_rows_kernel: 64 weight rows per workgroup (rows are independent),
 //     K in blocks of 64 columns: the contribution of all earlier residuals
-//     d_i to the block (a 64 x j0 x 64 product, four waves) and then the
-//     block's columns one after another (one lane per row);
+//     d_i to the block (a 64 x j0 x 64 product on the fp64 matrix cores,
+//     eight waves) and then the block's columns one after another (one lane
+//     per row);
 //  5. the codes are packed by the packing kernel.
 // deq_i = (q_i - z) * s is the exact value code q_i stands for.  The grid
 // (scales, zero points) is the RTN grid of the original weights
@@ -51,6 +52,7 @@ static_assert(kCB <= 64, "the diagonal block is factored by one wave");
 constexpr int kRows = 64;  // weight rows per GPTQ workgroup (32 on shorter layers)
 constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
 constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
+constexpr int kRowThreads = 512;  // step 4: eight waves, two per SIMD
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -255,14 +257,16 @@ __global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A
 // DT is the residual matrix transposed, DT[i][n] = d_i of row n, so that a
 // wave's loads of one column are contiguous.
 template <int RW>
-__global__ __launch_bounds__(256) void gptq_rows_kernel(
+__global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
     const uint16_t* __restrict__ w, int N, int K, const double* __restrict__ L,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int G, int gsz,
     int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
     uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
   static_assert(RW == 32 || RW == 64, "16-row product tiles, one lane per row");
-  constexpr int TU = RW / 32;                // 16-row product tiles per wave
+  constexpr int NRT = RW / 16;               // 16-row product tiles
+  constexpr int CPW = NRT / 2;               // 16-column product tiles per wave
+  static_assert(NRT * 4 == (kRowThreads / 64) * CPW, "one wave per group of product tiles");
   __shared__ double dsm[kChunk][RW];        // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][RW];            // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
   __shared__ uint32_t qs[RW][kNB / 4];       // the block's codes, stored together
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ml = lane & 15, kl = lane >> 4;
-  const int mb = (wave >> 1) * 16 * TU, nbw = (wave & 1) * 32;
+  const int mb = (wave % NRT) * 16, nbw = (wave / NRT) * 16 * CPW;
   const int r0 = blockIdx.x * RW;
   const int row = r0 + lane;
   const bool valid = lane < RW && row < N;
@@ -282,26 +286,26 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
   for (int jb = 0; jb < K; jb += kNB) {
     const int nb = min(kNB, K - jb);
     // contribution of the columns before the block, on the fp64 matrix
-    // cores: wave w sums rows mb .. mb + 16 TU - 1 and block columns
-    // nbw .. nbw + 31 as TU x 2 tiles of 16 x 16 (lane layout as in step 1)
-    f64x4_t acc[TU][2];
+    // cores: wave w sums rows mb .. mb + 15 and block columns
+    // nbw .. nbw + 16 CPW - 1 as 16 x 16 tiles (lane layout as in step 1);
+    // two waves per SIMD keep the matrix pipe busier than one
+    f64x4_t acc[CPW];
 #pragma unroll
-    for (int u = 0; u < TU; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v) acc[u][v] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    for (int v = 0; v < CPW; ++v) acc[v] = f64x4_t{0.0, 0.0, 0.0, 0.0};
     // Chunks of 64 earlier columns: R rows and residuals staged in LDS, the
     // next chunk's loads issued (into registers) before this chunk's products.
     const int nchunks = jb / kChunk;
-    double pr[16], pd[RW / 4];
+    constexpr int PR = kChunk * kNB / kRowThreads, PD = kChunk * RW / kRowThreads;
+    double pr[PR], pd[PD];
     auto fetch = [&](int i0) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
+      for (int k = 0; k < PR; ++k) {
+        const int e = tid + kRowThreads * k, ii = e >> 6, c = e & 63;
         pr[k] = c < nb ? Rat(i0 + ii, jb + c) : 0.0;
       }
 #pragma unroll
-      for (int k = 0; k < RW / 4; ++k) {
-        const int e = tid + 256 * k, ii = e / RW, c = e % RW;
+      for (int k = 0; k < PD; ++k) {
+        const int e = tid + kRowThreads * k, ii = e / RW, c = e % RW;
         pd[k] = r0 + c < N ? DT[(int64_t)(i0 + ii) * N + r0 + c] : 0.0;
       }
     };
@@ -309,13 +313,13 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     for (int ch = 0; ch < nchunks; ++ch) {
       __syncthreads();  // the previous chunk has been read
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int e = tid + 256 * k, ii = e >> 6, c = e & 63;
+      for (int k = 0; k < PR; ++k) {
+        const int e = tid + kRowThreads * k, ii = e >> 6, c = e & 63;
         rs[ii][c] = pr[k];
       }
 #pragma unroll
-      for (int k = 0; k < RW / 4; ++k) {
-        const int e = tid + 256 * k, ii = e / RW, c = e % RW;
+      for (int k = 0; k < PD; ++k) {
+        const int e = tid + kRowThreads * k, ii = e / RW, c = e % RW;
         dsm[ii][c] = pd[k];
       }
       __syncthreads();
@@ -323,32 +327,27 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
 #pragma unroll
       for (int kk = 0; kk < kChunk / 4; ++kk) {
         const int ii = 4 * kk + kl;
-        double a[TU], b[2];
+        const double a = dsm[ii][mb + ml];
+        double b[CPW];
 #pragma unroll
-        for (int u = 0; u < TU; ++u) a[u] = dsm[ii][mb + 16 * u + ml];
+        for (int v = 0; v < CPW; ++v) b[v] = rs[ii][nbw + 16 * v + ml];
 #pragma unroll
-        for (int v = 0; v < 2; ++v) b[v] = rs[ii][nbw + 16 * v + ml];
-#pragma unroll
-        for (int u = 0; u < TU; ++u)
-#pragma unroll
-          for (int v = 0; v < 2; ++v)
-            acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[u], b[v], acc[u][v], 0, 0, 0);
+        for (int v = 0; v < CPW; ++v)
+          acc[v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[v], acc[v], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int u = 0; u < TU; ++u)
+    for (int v = 0; v < CPW; ++v)
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + 16 * u + kl + 4 * e] = acc[u][v][e];
-    for (int e = tid; e < kNB * kNB; e += 256) {
+      for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + kl + 4 * e] = acc[v][e];
+    for (int e = tid; e < kNB * kNB; e += kRowThreads) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
     }
     // the reciprocals of the block's diagonal, so the column walk's chain
     // holds one division (the code decision) instead of two
-    for (int a = tid; a < kNB; a += 256) rdi[a] = a < nb ? 1.0 / Rat(jb + a, jb + a) : 1.0;
-    for (int e = tid; e < RW * kNB; e += 256) {
+    for (int a = tid; a < kNB; a += kRowThreads) rdi[a] = a < nb ? 1.0 / Rat(jb + a, jb + a) : 1.0;
+    for (int e = tid; e < RW * kNB; e += kRowThreads) {
       const int rr = e / kNB, c = e % kNB;
       ws[rr][c] = (r0 + rr < N && c < nb) ? w[(int64_t)(r0 + rr) * K + jb + c] : (uint16_t)0;
     }
@@ -405,7 +404,7 @@ __global__ __launch_bounds__(256) void gptq_rows_kernel(
     }
     __syncthreads();
     // the block's codes, four per store (K is a multiple of 32, jb of 64)
-    for (int e = tid; e < RW * (kNB / 4); e += 256) {
+    for (int e = tid; e < RW * (kNB / 4); e += kRowThreads) {
       const int rr = e / (kNB / 4), c4 = e % (kNB / 4);
       if (r0 + rr < N && 4 * c4 < nb)
         *reinterpret_cast<uint32_t*>(codes + (int64_t)(r0 + rr) * K + jb + 4 * c4) = qs[rr][c4];
@@ -512,10 +511,10 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   // 11008-row layer than 64).
   const int qmax = (1 << bits) - 1, qlo = sym ? 1 : 0;
   if ((n + 31) / 32 <= device_cu_count())
-    hipLaunchKernelGGL(gptq_rows_kernel<32>, dim3((n + 31) / 32), dim3(256), 0, stream, w, n, k, A,
+    hipLaunchKernelGGL(gptq_rows_kernel<32>, dim3((n + 31) / 32), dim3(kRowThreads), 0, stream, w, n, k, A,
                        scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
   else
-    hipLaunchKernelGGL(gptq_rows_kernel<kRows>, dim3((n + kRows - 1) / kRows), dim3(256), 0,
+    hipLaunchKernelGGL(gptq_rows_kernel<kRows>, dim3((n + kRows - 1) / kRows), dim3(kRowThreads), 0,
                        stream, w, n, k, A, scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
