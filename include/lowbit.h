@@ -207,9 +207,12 @@ LOWBIT_API int lowbit_qgemm_meta(const void* x_f16, int64_t B, const uint32_t* p
  * The computation runs in fp64 in the caller's device workspace of at least
  * lowbit_gptq_workspace_bytes(N, K) bytes (256-byte aligned; returns a
  * negative status for invalid sizes).  On return of the work its first int32
- * is 0, or 1 when H was not positive definite (all calibration inputs zero),
- * in which case the codes are unspecified.  Calls on one workspace must not
- * overlap.  The library allocates nothing.
+ * is 0, or has bit value 1 set when H was not positive definite (all
+ * calibration inputs zero), in which case the codes are unspecified; bit
+ * value 2 would report that the factorization stopped waiting for a tile
+ * after its bound (not expected to occur; the codes are then unspecified as
+ * well).  Calls on one workspace must not overlap.  The library allocates
+ * nothing.
  */
 LOWBIT_API int64_t lowbit_gptq_workspace_bytes(int64_t N, int64_t K);
 LOWBIT_API int lowbit_quantize_gptq(const void* w_f16, int64_t N, int64_t K, const void* x_f16,
@@ -245,8 +248,8 @@ LOWBIT_API int lowbit_quantize_gptq_sym(const void* w_f16, int64_t N, int64_t K,
  * LOWBIT_GPTQ_NOALLOC_MAX_BYTES per GPU, held from the first call on that GPU
  * until the process ends.  A problem whose lowbit_gptq_workspace_bytes(N, K)
  * exceeds it returns LOWBIT_ERR_SCRATCH before anything is enqueued (e.g.
- * N = K = 2048 fits; N = 11008, K = 4096 does not).  The status word (0, or
- * 1 when H was not positive definite) is written to *status_or_null (a
+ * N = K = 2048 fits; N = 11008, K = 4096 does not).  The status word (as
+ * for lowbit_quantize_gptq) is written to *status_or_null (a
  * 4-byte aligned device int32 owned by the caller; NULL: not reported).
  * This entry point allocates nothing and calls no allocating routine.  All
  * calls on one GPU share the array and each call overwrites what the

@@ -199,6 +199,8 @@ def test_gptq_noalloc_scratch_bound(lw):
 def test_gptq_workspace_size(lw):
     K, N = 4096, 11008
     up = lambda b: (b + 255) // 256 * 256
-    assert lw.gptq_workspace_bytes(N, K) == 256 + up(K * K * 8) + up(K * N * 8) + up(N * K)
+    nt = (K + 63) // 64  # 64 x 64 Cholesky tiles per side, one int32 counter each
+    assert lw.gptq_workspace_bytes(N, K) == (256 + up(K * K * 8) + up(K * N * 8) + up(N * K)
+                                             + up(nt * nt * 4))
     assert lw.gptq_workspace_bytes(-1, K) < 0
     assert lw.gptq_workspace_bytes(N, 0) < 0

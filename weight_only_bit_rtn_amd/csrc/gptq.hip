@@ -23,10 +23,9 @@
 //  1. hessian_kernel: reverse(H) = (2/n) X^T X with both indices reversed
 //     (the lower triangle, which is all the later steps read);
 //  2. damp_kernel: damp * mean(diag) added to the diagonal; status cleared;
-//  3. right-looking blocked Cholesky of reverse(H) in place, 32 columns per
-//     panel: diagonal block in one workgroup (chol_diag_kernel), the panel
-//     below by row-wise substitution (chol_panel_kernel), the trailing lower
-//     triangle by 64x64 tiles (chol_update_kernel);
+//  3. chol_tiles_kernel: tiled right-looking Cholesky of reverse(H) in
+//     place, 64 x 64 tiles, one launch: workgroups take the factor, solve and
+//     update tasks in dependency order and wait only for the tiles they read;
 //  4. gptq_rows_kernel: 64 weight rows per workgroup (rows are independent),
 //     K in blocks of 64 columns: the contribution of all earlier residuals
 //     d_i to the block (a 64 x j0 x 64 product on the fp64 matrix cores,
@@ -47,8 +46,6 @@ namespace lowbit {
 namespace {
 
 constexpr int kNB = 64;    // GPTQ column block
-constexpr int kCB = 32;    // Cholesky panel width (one lane per row of the diagonal block)
-static_assert(kCB <= 64, "the diagonal block is factored by one wave");
 constexpr int kRows = 64;  // weight rows per GPTQ workgroup (32 on shorter layers)
 constexpr int kChunk = 64;   // earlier columns staged per LDS round in step 4
 constexpr int kHChunk = 32;  // calibration rows staged per LDS round in step 1
@@ -117,9 +114,14 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
       }
 }
 
-// Step 2 (one workgroup): diag += damp * trace / K; the status word is cleared.
+// Step 2 (one workgroup): diag += damp * trace / K; the status word, the
+// task counter and the tile counters of step 3 are cleared.
 __global__ __launch_bounds__(1024) void damp_kernel(double* __restrict__ A, int K, double damp,
-                                                    int32_t* __restrict__ status) {
+                                                    int32_t* __restrict__ status,
+                                                    int* __restrict__ ver, int nver,
+                                                    int* __restrict__ ticket) {
+  for (int i = threadIdx.x; i < nver; i += blockDim.x) ver[i] = 0;
+  if (threadIdx.x == 0) ticket[0] = 0;
   __shared__ double part[1024];
   double s = 0.0;
   for (int i = threadIdx.x; i < K; i += blockDim.x) s += A[(int64_t)i * K + i];
@@ -134,122 +136,353 @@ __global__ __launch_bounds__(1024) void damp_kernel(double* __restrict__ A, int 
   if (threadIdx.x == 0) status[0] = 0;
 }
 
-// Step 3a (one workgroup): Cholesky of the nb x nb diagonal block at kb.  A
-// non-positive pivot (H not positive definite) sets the status word and is
-// replaced by 1 so that the remaining steps stay finite.
-// One wave, lane r holding row r of the block in registers.  Step c: the
-// pivot comes from lane c, lanes below scale their entry of column c, the
-// column goes through LDS, and every lane updates its row (entries right of
-// its diagonal are never used).
-__global__ __launch_bounds__(64) void chol_diag_kernel(double* __restrict__ A, int K, int kb,
-                                                       int nb, int32_t* __restrict__ status) {
-  __shared__ double col[kCB];
-  const int r = threadIdx.x;
-  double a[kCB];
+// Step 3, as one kernel over 64 x 64 tiles of the lower triangle (nt tiles
+// per side): the tasks of the right-looking tiled Cholesky,
+//   for k: factor tile (k, k); solve tiles (i, k), i > k, against it;
+//          update tiles (i, j), k < j <= i, by tile(i, k) tile(j, k)^T,
+// numbered in that order (within step k the updates column by column, so
+// that tile (k+1, k+1), which the next factorization needs, comes first).
+// Workgroups take task numbers from a counter and wait only for the tiles
+// their task reads: ver[i nt + j] counts the updates applied to tile (i, j),
+// plus one once it is final.  Every task waits only for tasks with smaller
+// numbers, which workgroups that are already running hold, so the waits end;
+// each is bounded all the same (status bit 2 if a bound is ever reached, and
+// every later wait then gives up at once).
+// Tiles move between workgroups through device-coherent loads and stores
+// (they bypass the non-coherent caches), so a tile is published by waiting
+// for its stores and then storing its counter; no cache-wide write-back or
+// invalidation is needed.
+constexpr int kT = 64;
+constexpr int kTP = kT + 2;  // LDS tile row stride: 16-byte aligned rows
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ double ld_dev(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every earlier memory operation of this wave has completed (vmcnt = 0)
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)b, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// 1 / sqrt(d) to fp64 accuracy: the hardware estimate and two Newton steps
+__device__ __forceinline__ double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  y = y * (1.5 - 0.5 * d * y * y);
+  y = y * (1.5 - 0.5 * d * y * y);
+  return y;
+}
+
+int chol_task_count(int nt) {
+  int n = 0;
+  for (int k = 0; k < nt; ++k) {
+    const int m = nt - 1 - k;
+    n += 1 + m + m * (m + 1) / 2;
+  }
+  return n;
+}
+
+// a[m] -= x * v[m] for m in (C, kT), v an LDS row, in batches of eight: the
+// reads of the next batch go out before the multiply-adds of this one, and
+// scheduling barriers keep the compiler from hoisting further reads (at the
+// register limit it would park them in scratch).  Plain double reads, which
+// the compiler pairs, keep their order with the stores to v.
+template <int C>
+__device__ __forceinline__ void axpy_tail(double (&a)[kT], double x, const double* v) {
+  constexpr int kB0 = (C + 1) & ~1;
+  constexpr int kNBat = (kT - kB0 + 7) / 8;
+  double cur[8], nxt[8];
 #pragma unroll
-  for (int c = 0; c < kCB; ++c)
-    a[c] = (r < nb && c < nb) ? A[(int64_t)(kb + r) * K + kb + c] : (c == r ? 1.0 : 0.0);
+  for (int t = 0; t < 8; ++t)
+    if (kB0 + t < kT) cur[t] = v[kB0 + t];
 #pragma unroll
-  for (int c = 0; c < kCB; ++c) {
-    if (c < nb) {
-      double d = __shfl(a[c], c);
-      if (!(d > 0.0)) {
-        if (r == 0) status[0] = 1;
-        d = 1.0;
+  for (int bi = 0; bi < kNBat; ++bi) {
+    const int mb = kB0 + 8 * bi;
+    if (bi + 1 < kNBat) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (mb + 8 + t < kT) nxt[t] = v[mb + 8 + t];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (mb + t > C && mb + t < kT) a[mb + t] = __builtin_fma(-x, cur[t], a[mb + t]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
+  }
+}
+
+// Branch-free steps (one basic block, so that no multiply-add is sunk into a
+// later step with its operand held live); a non-positive pivot is replaced
+// by 1 and counted in bad.
+template <int C>
+__device__ __forceinline__ void potrf_steps(double (&a)[kT], int r, double* col, int& bad) {
+  if constexpr (C < kT) {
+    double d = readlane_f64(a[C], C);
+    const bool ok = d > 0.0;  // d is the same in every lane
+    bad |= ok ? 0 : 1;
+    d = ok ? d : 1.0;
+    const double rp = rsqrt_f64(d);
+    // rows r >= C: the factor's entry (d rp on the diagonal); rows r < C
+    // hold entries above their diagonal here, which are never read
+    const double l = a[C] * rp;
+    a[C] = l;
+    // column C through LDS; the opaque offset keeps this step's reads after
+    // its own write
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    double* cp = col + off;
+    cp[r] = l;
+    __builtin_amdgcn_wave_barrier();
+    // rows r < k receive updates of entries above their diagonal, which are
+    // never read: no per-lane condition
+    axpy_tail<C>(a, l, cp);
+    __builtin_amdgcn_wave_barrier();
+    potrf_steps<C + 1>(a, r, col, bad);
+  }
+}
+
+template <int C>
+__device__ __forceinline__ void trsm_steps(double (&a)[kT], const double* lt, const double* rd) {
+  if constexpr (C < kT) {
+    const double x = a[C] * rd[C];
+    a[C] = x;
+    // the row offset is made to depend on x, so that this step's reads are
+    // not hoisted ahead of the steps before it
+    int off = C * kTP;
+    asm volatile("" : "+v"(off) : "v"(x));
+    axpy_tail<C>(a, x, lt + off);
+    trsm_steps<C + 1>(a, lt, rd);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__ A, int K, int nt,
+                                                            int ntasks, int* __restrict__ ver,
+                                                            int* __restrict__ ticket,
+                                                            int32_t* __restrict__ status) {
+  __shared__ __align__(16) double ta[kT][kTP];
+  __shared__ __align__(16) double tb[kT][kTP];
+  __shared__ __align__(16) double rd[kT];
+  __shared__ int task[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // No control flow in this loop depends on the lane: wave 0 as a whole
+  // takes the task and waits, the other waves wait at the barrier.  (With a
+  // thread-0 region at each end of the loop body, the two regions can be
+  // merged across the back edge into a loop exit that the other lanes of
+  // wave 0 do not take; they then meet the next barrier without thread 0.)
+  for (;;) {
+    if (wave == 0) {
+      int t = 0;
+      if (lane == 0) t = atomicAdd(ticket, 1);
+      t = __builtin_amdgcn_readfirstlane(t);  // lane 0, the first active lane
+      int type = -1, ti = 0, tj = 0, tk = 0;
+      if (t < ntasks) {
+        int k = 0, base = 0, m = nt - 1;
+        for (;;) {
+          const int sz = 1 + m + m * (m + 1) / 2;
+          if (t < base + sz) break;
+          base += sz, ++k, --m;
+        }
+        const int o = t - base;
+        if (o == 0) {
+          type = 0, ti = tj = tk = k;
+        } else if (o <= m) {
+          type = 1, ti = k + o, tj = k, tk = k;
+        } else {
+          int u = o - 1 - m, j = k + 1;
+          while (u >= nt - j) u -= nt - j, ++j;
+          type = 2, ti = j + u, tj = j, tk = k;
+        }
+        // every lane polls the same word; the value is taken from lane 0
+        auto wait_ge = [&](int idx, int target) {
+          for (int it = 0;; ++it) {
+            const int v = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(&ver[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (v >= target) return;
+            if ((it & 63) == 63 &&
+                (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                     status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 2))
+              return;
+            if (it >= kSpinLimit) {
+              atomicOr(status, 2);
+              return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        };
+        wait_ge(ti * nt + tj, tk);  // the earlier updates of the task's own tile
+        if (type == 1) wait_ge(tk * nt + tk, tk + 1);
+        if (type == 2) {
+          wait_ge(ti * nt + tk, tk + 1);
+          wait_ge(tj * nt + tk, tk + 1);
+        }
+        // the tile loads below are issued after the counters were seen
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
-      const double p = __builtin_sqrt(d);
-      const double lrc = r > c ? a[c] / p : (r == c ? p : a[c]);
-      a[c] = lrc;
-      col[r] = lrc;
+      // all lanes write the same values
+      task[0] = type, task[1] = ti, task[2] = tj, task[3] = tk;
+    }
+    __syncthreads();
+    const int type = __builtin_amdgcn_readfirstlane(task[0]);
+    const int ti = __builtin_amdgcn_readfirstlane(task[1]);
+    const int tj = __builtin_amdgcn_readfirstlane(task[2]);
+    const int tk = __builtin_amdgcn_readfirstlane(task[3]);
+    if (type < 0) return;
+    const int r0 = ti * kT, c0 = tj * kT, k0 = tk * kT;
+    const int nbi = min(kT, K - r0), nbj = min(kT, K - c0);
+    // The thread index, opaque per task: values derived from it are
+    // recomputed in each task instead of being held (and spilled) across
+    // the whole loop.
+    int tid_ = tid;
+    asm volatile("" : "+v"(tid_));
+    const int lane = tid_ & 63;
+    // Staging: thread tid handles entries (4 q + tid / 64, tid % 64), q < 16;
+    // rows past the matrix are clamped for the load and replaced by 0 (or
+    // the identity) afterwards, so every load is issued unconditionally.
+    const int er = tid_ >> 6, ec = tid_ & 63;
+    if (type == 0) {
+      // factor tile (k, k): one wave, lane r holding row r; column c's
+      // entries go through LDS to every lane
+      double v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + er;
+        v[q] = ld_dev(&A[(int64_t)(r0 + min(r, nbi - 1)) * K + r0 + min(ec, nbi - 1)]);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + er;
+        ta[r][ec] = (r < nbi && ec <= r) ? v[q] : (r == ec ? 1.0 : 0.0);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int r = lane;
+        double a[kT];
+#pragma unroll
+        for (int c = 0; c < kT; c += 2) {
+          const double2 w = *reinterpret_cast<const double2*>(&ta[r][c]);
+          a[c] = w.x, a[c + 1] = w.y;
+        }
+        int bad = 0;
+        potrf_steps<0>(a, r, rd, bad);
+        if (bad) atomicOr(status, 1);  // the same in every lane
+#pragma unroll
+        for (int c = 0; c < kT; ++c) ta[r][c] = a[c];
+      }
       __syncthreads();
 #pragma unroll
-      for (int k = c + 1; k < kCB; ++k)
-        if (r >= k) a[k] -= lrc * col[k];
+      for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + er;
+        if (r < nbi && ec <= r) st_dev(&A[(int64_t)(r0 + r) * K + r0 + ec], ta[r][ec]);
+      }
+    } else if (type == 1) {
+      // solve tile (i, k): X L_kk^T = A_ik, one wave, lane r holding row r;
+      // ta[c][m] = L_kk[m][c] (column c of the factor as a row)
+      double v[16], w[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = 4 * q + er;
+        v[q] = ld_dev(&A[(int64_t)(k0 + m) * K + k0 + ec]);
+        w[q] = ld_dev(&A[(int64_t)(r0 + min(m, nbi - 1)) * K + k0 + ec]);
+      }
+      double dg = 1.0;
+      if (tid < kT) dg = ld_dev(&A[(int64_t)(k0 + tid) * K + k0 + tid]);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = 4 * q + er;
+        ta[ec][m] = ec <= m ? v[q] : 0.0;
+        tb[m][ec] = m < nbi ? w[q] : 0.0;
+      }
+      if (tid < kT) rd[tid] = 1.0 / dg;
       __syncthreads();
+      if (wave == 0) {
+        double a[kT];
+#pragma unroll
+        for (int c = 0; c < kT; c += 2) {
+          const double2 x2 = *reinterpret_cast<const double2*>(&tb[lane][c]);
+          a[c] = x2.x, a[c + 1] = x2.y;
+        }
+        trsm_steps<0>(a, &ta[0][0], rd);
+#pragma unroll
+        for (int c = 0; c < kT; ++c) tb[lane][c] = a[c];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = 4 * q + er;
+        if (m < nbi) st_dev(&A[(int64_t)(r0 + m) * K + k0 + ec], tb[m][ec]);
+      }
+    } else {
+      // update tile (i, j) -= tile(i, k) tile(j, k)^T on the fp64 matrix
+      // cores: wave w owns the 32 x 32 quarter (w / 2, w % 2) as 2 x 2 tiles
+      const int ml = lane & 15, kl = lane >> 4;
+      const int mb = (wave >> 1) * 32, nbw = (wave & 1) * 32;
+      double v[16], w[16];
+      f64x4_t acc[2][2];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + er;
+        v[q] = ld_dev(&A[(int64_t)(r0 + min(r, nbi - 1)) * K + k0 + ec]);
+        w[q] = ld_dev(&A[(int64_t)(c0 + min(r, nbj - 1)) * K + k0 + ec]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int vv = 0; vv < 2; ++vv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = mb + 16 * u + kl + 4 * e, c = nbw + 16 * vv + ml;
+            acc[u][vv][e] =
+                ld_dev(&A[(int64_t)(r0 + min(r, nbi - 1)) * K + c0 + min(c, nbj - 1)]);
+          }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = 4 * q + er;
+        ta[r][ec] = r < nbi ? v[q] : 0.0;
+        tb[r][ec] = r < nbj ? w[q] : 0.0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kT / 4; ++kk) {
+        const int m = 4 * kk + kl;
+        const double a0 = -ta[mb + ml][m], a1 = -ta[mb + 16 + ml][m];
+        const double b0 = tb[nbw + ml][m], b1 = tb[nbw + 16 + ml][m];
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int vv = 0; vv < 2; ++vv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = mb + 16 * u + kl + 4 * e, c = nbw + 16 * vv + ml;
+            if (r < nbi && c < nbj && (ti != tj || c <= r))
+              st_dev(&A[(int64_t)(r0 + r) * K + c0 + c], acc[u][vv][e]);
+          }
     }
+    // publish the tile: every wave's stores have completed before the
+    // counter moves
+    wait_vmem();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (wave == 0)  // every lane stores the same value
+      __hip_atomic_store(&ver[ti * nt + tj], tk + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (r < nb) {
-#pragma unroll
-    for (int c = 0; c < kCB; ++c)
-      if (c <= r) A[(int64_t)(kb + r) * K + kb + c] = a[c];
-  }
-}
-
-// Step 3b: rows below the diagonal block, one row per thread: solve
-// x L11^T = a (forward substitution) for the row's nb panel entries.
-__global__ __launch_bounds__(256) void chol_panel_kernel(double* __restrict__ A, int K, int kb,
-                                                         int nb) {
-  __shared__ double l[kCB][kCB + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < nb * nb; e += 256) {
-    const int r = e / nb, c = e % nb;
-    l[r][c] = c <= r ? A[(int64_t)(kb + r) * K + kb + c] : 0.0;
-  }
-  __syncthreads();
-  const int r = kb + nb + blockIdx.x * 256 + tid;
-  if (r >= K) return;
-  double* row = A + (int64_t)r * K + kb;
-  double v[kCB];
-#pragma unroll
-  for (int c = 0; c < kCB; ++c) v[c] = c < nb ? row[c] : 0.0;
-#pragma unroll
-  for (int c = 0; c < kCB; ++c) {
-    if (c < nb) {
-      // four partial sums: a quarter of the dependent chain
-      double s4[4] = {v[c], 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int k = 0; k < c; ++k) s4[k & 3] -= v[k] * l[c][k];
-      v[c] = ((s4[0] + s4[1]) + (s4[2] + s4[3])) / l[c][c];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < kCB; ++c)
-    if (c < nb) row[c] = v[c];
-}
-
-// Step 3c: trailing lower triangle from s0 = kb + nb on: A[i][j] -= sum_k
-// L[i][kb + k] L[j][kb + k], in 64 x 64 tiles (ti >= tj), one workgroup per
-// tile of the lower triangle.
-__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A, int K, int kb,
-                                                          int nb) {
-  // workgroup p takes tile (ti, tj) of the lower triangle, p = ti (ti + 1) / 2 + tj
-  const int p = (int)blockIdx.x;
-  int ti = (int)((__builtin_sqrtf(8.0f * (float)p + 1.0f) - 1.0f) * 0.5f);
-  while ((ti + 1) * (ti + 2) / 2 <= p) ++ti;
-  while (ti * (ti + 1) / 2 > p) --ti;
-  const int tj = p - ti * (ti + 1) / 2;
-  __shared__ double li[64][kCB + 1];
-  __shared__ double lj[64][kCB + 1];
-  const int s0 = kb + nb;
-  const int i0 = s0 + 64 * ti, j0 = s0 + 64 * tj;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  for (int e = tid; e < 64 * kCB; e += 256) {
-    const int r = e / kCB, k = e % kCB;
-    li[r][k] = (i0 + r < K && k < nb) ? A[(int64_t)(i0 + r) * K + kb + k] : 0.0;
-    lj[r][k] = (j0 + r < K && k < nb) ? A[(int64_t)(j0 + r) * K + kb + k] : 0.0;
-  }
-  __syncthreads();
-  double acc[4][4] = {};
-#pragma unroll 4
-  for (int k = 0; k < kCB; ++k) {
-    double a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = li[4 * ty + u][k];
-      b[u] = lj[4 * tx + u][k];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = i0 + 4 * ty + u, j = j0 + 4 * tx + v;
-      if (i < K && j <= i) A[(int64_t)i * K + j] -= acc[u][v];
-    }
 }
 
 // Step 4.  Workgroup b owns rows r0 = RW b .. r0 + RW - 1 (lane = row; RW is
@@ -467,7 +700,9 @@ hipError_t launch_gptq_noalloc(const uint16_t* w, int64_t N, int64_t K, const ui
 
 size_t gptq_workspace_bytes(int64_t N, int64_t K) {
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  return 256 + up((size_t)K * K * 8) + up((size_t)K * N * 8) + up((size_t)N * K);
+  const size_t nt = (size_t)((K + kT - 1) / kT);
+  return 256 + up((size_t)K * K * 8) + up((size_t)K * N * 8) + up((size_t)N * K) +
+         up(nt * nt * 4);
 }
 
 hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* x,
@@ -480,6 +715,8 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   double* A = reinterpret_cast<double*>(base + 256);
   double* DT = reinterpret_cast<double*>(base + 256 + up((size_t)K * K * 8));
   uint8_t* wcodes = base + 256 + up((size_t)K * K * 8) + up((size_t)K * N * 8);
+  int* ver = reinterpret_cast<int*>(wcodes + up((size_t)N * K));
+  int* ticket = reinterpret_cast<int*>(base + 64);
   uint8_t* out_codes = codes ? codes : wcodes;
   const int k = (int)K, n = (int)N;
 
@@ -490,19 +727,11 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
   const int tiles = (k + 63) / 64;
   hipLaunchKernelGGL(hessian_kernel, dim3(tiles, tiles), dim3(256), 0, stream, x, n_samples, k,
                      A);
-  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, A, k, damp, status);
-  for (int kb = 0; kb < k; kb += kCB) {
-    const int nb = k - kb < kCB ? k - kb : kCB;
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kCB), 0, stream, A, k, kb, nb, status);
-    const int below = k - kb - nb;
-    if (below > 0) {
-      hipLaunchKernelGGL(chol_panel_kernel, dim3((below + 255) / 256), dim3(256), 0, stream, A,
-                         k, kb, nb);
-      const int t = (below + 63) / 64;
-      hipLaunchKernelGGL(chol_update_kernel, dim3(t * (t + 1) / 2), dim3(256), 0, stream, A, k, kb,
-                         nb);
-    }
-  }
+  const int nt = (k + kT - 1) / kT;
+  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, stream, A, k, damp, status, ver,
+                     nt * nt, ticket);
+  hipLaunchKernelGGL(chol_tiles_kernel, dim3(2 * device_cu_count()), dim3(256), 0, stream, A, k,
+                     nt, chol_task_count(nt), ver, ticket, status);
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
   // Rows per workgroup: 32 when those workgroups all run at once (one per
