@@ -71,8 +71,8 @@ __device__ __forceinline__ double h_bits_to_f64(uint16_t b) {
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                       int K, double* __restrict__ Hrev) {
   if (blockIdx.x > blockIdx.y) return;
-  __shared__ double xi[kHChunk][64];
-  __shared__ double xj[kHChunk][64];
+  __shared__ __align__(16) double xi[kHChunk][64];
+  __shared__ __align__(16) double xj[kHChunk][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
   const int ml = lane & 15, kl = lane >> 4;
@@ -82,25 +82,48 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t* __restrict
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v) acc[u][v] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  for (int64_t t0 = 0; t0 < n; t0 += kHChunk) {
-    for (int e = tid; e < kHChunk * 64; e += 256) {
-      const int tt = e >> 6, c = e & 63;
-      const int64_t t = t0 + tt;
-      xi[tt][c] = (t < n && i0 + c < K) ? h_bits_to_f64(x[t * K + i0 + c]) : 0.0;
-      xj[tt][c] = (t < n && j0 + c < K) ? h_bits_to_f64(x[t * K + j0 + c]) : 0.0;
+  // Staging: each thread brings 8 consecutive values (16 bytes) of one
+  // calibration row for each operand (K is a multiple of 32 and x 16-byte
+  // aligned, so a piece is wholly inside or outside the matrix); the next
+  // chunk's pieces are loaded while this chunk multiplies.  Rows past n and
+  // columns past K are clamped for the load and replaced by zeros.
+  static_assert(kHChunk * 8 == 256, "one 16-byte piece per thread and operand");
+  const int tt = tid >> 3, c8 = (tid & 7) * 8;
+  const bool in_i = i0 + c8 < K, in_j = j0 + c8 < K;
+  const int ci = in_i ? i0 + c8 : 0, cj = in_j ? j0 + c8 : 0;
+  uint4 pi, pj;
+  auto fetch = [&](int64_t t0) {
+    const int64_t t = t0 + tt < n ? t0 + tt : n - 1;
+    pi = *reinterpret_cast<const uint4*>(x + t * K + ci);
+    pj = *reinterpret_cast<const uint4*>(x + t * K + cj);
+  };
+  auto put = [&](double (*dst)[64], uint4 p, bool keep) {
+    const uint32_t wv[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double lo = keep ? h_bits_to_f64((uint16_t)(wv[q] & 0xffffu)) : 0.0;
+      const double hi = keep ? h_bits_to_f64((uint16_t)(wv[q] >> 16)) : 0.0;
+      *reinterpret_cast<double2*>(&dst[tt][c8 + 2 * q]) = double2{lo, hi};
     }
+  };
+  fetch(0);
+  for (int64_t t0 = 0; t0 < n; t0 += kHChunk) {
+    const bool row_in = t0 + tt < n;
+    __syncthreads();  // the previous chunk has been read
+    put(xi, pi, row_in && in_i);
+    put(xj, pj, row_in && in_j);
     __syncthreads();
+    if (t0 + kHChunk < n) fetch(t0 + kHChunk);
 #pragma unroll
     for (int kk = 0; kk < kHChunk / 4; ++kk) {
-      const int tt = 4 * kk + kl;
-      const double a0 = xi[tt][mb + ml], a1 = xi[tt][mb + 16 + ml];
-      const double b0 = xj[tt][nbw + ml], b1 = xj[tt][nbw + 16 + ml];
+      const int tt4 = 4 * kk + kl;
+      const double a0 = xi[tt4][mb + ml], a1 = xi[tt4][mb + 16 + ml];
+      const double b0 = xj[tt4][nbw + ml], b1 = xj[tt4][nbw + 16 + ml];
       acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
-    __syncthreads();
   }
   const double f = 2.0 / (double)n;
 #pragma unroll
