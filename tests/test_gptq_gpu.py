@@ -6,7 +6,7 @@ code in fp64; they compute the running weights in different (algebraically
 equal) ways, so a code could differ only where a quotient falls within about
 1e-12 of a rounding midpoint, which seeded continuous inputs do not produce.
 Shapes cover K that is not a multiple of the 64-column block, ragged row
-tiles (32- and 64-row workgroups), every width, per-row and grouped grids (power-of-two and other group
+tiles (32-, 48- and 64-row workgroups), every width, per-row and grouped grids (power-of-two and other group
 sizes), and one workload layer at full size (every row through the oracle).
 """
 from __future__ import annotations
@@ -74,9 +74,10 @@ def _check(lw, w, x, bits, g, damp, what, codes=True, packed=True, symmetric=Fal
     return rc
 
 
-# The row kernel takes 32 rows per workgroup when those workgroups all fit on
-# the CUs at once (256 on MI355X), else 64: the 8200- and 16448-row shapes
-# take the 64-row form, all others the 32-row form.
+# The row kernel takes the fewest of 32, 48 and 64 rows per workgroup whose
+# workgroups all fit on the CUs at once (256 on MI355X): the 8200-row shapes
+# take the 48-row form (ragged: 8200 = 170 * 48 + 40), the 16448-row shapes
+# the 64-row form, all others the 32-row form.
 CASES = [(5, 32, 4, 0), (17, 128, 3, 0), (64, 192, 2, 32), (67, 128, 4, 64), (130, 96, 8, 0),
          (70, 160, 4, 32), (33, 352, 4, 0), (129, 512, 3, 128), (40, 480, 4, 96),
          (21, 320, 2, 64), (66, 256, 8, 32), (8200, 96, 4, 32), (8200, 320, 2, 0), (16448, 128, 3, 0),

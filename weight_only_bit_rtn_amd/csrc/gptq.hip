@@ -37,6 +37,7 @@
 // (min-max, or signed symmetric with codes from 1), written by the RTN
 // quantizer before step 4.
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -197,14 +198,6 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// 1 / sqrt(d) to fp64 accuracy: the hardware estimate and two Newton steps
-__device__ __forceinline__ double rsqrt_f64(double d) {
-  double y = __builtin_amdgcn_rsq(d);
-  y = y * (1.5 - 0.5 * d * y * y);
-  y = y * (1.5 - 0.5 * d * y * y);
-  return y;
-}
-
 int chol_task_count(int nt) {
   int n = 0;
   for (int k = 0; k < nt; ++k) {
@@ -214,77 +207,138 @@ int chol_task_count(int nt) {
   return n;
 }
 
-// a[m] -= x * v[m] for m in (C, kT), v an LDS row, in batches of eight: the
-// reads of the next batch go out before the multiply-adds of this one, and
-// scheduling barriers keep the compiler from hoisting further reads (at the
-// register limit it would park them in scratch).  Plain double reads, which
-// the compiler pairs, keep their order with the stores to v.
+// The factor and solve tasks run one wave over the 64 rows of a tile (lane r
+// holding row r in registers).  Step C updates the entries m > C of every
+// row with column C: a[m] -= x a_C[m], the a_C[m] read from LDS (broadcast)
+// in batches of eight.  Both are software-pipelined by hand: the reads of
+// the next batch (across step boundaries) go out before the multiply-adds of
+// this one, and in the factorization the next pivot's dependent chain
+// (pivot, reciprocal square root, scaling, LDS write) is spread over the
+// batches of the current step, whose first batch already finishes column
+// C + 1.  Scheduling barriers keep that order (left to itself, at the
+// register limit the compiler hoists every read and parks them in scratch).
+// Plain double reads, which the compiler pairs, keep their order with the
+// LDS stores to the same buffer.
 template <int C>
-__device__ __forceinline__ void axpy_tail(double (&a)[kT], double x, const double* v) {
-  constexpr int kB0 = (C + 1) & ~1;
-  constexpr int kNBat = (kT - kB0 + 7) / 8;
-  double cur[8], nxt[8];
+struct StepShape {
+  static constexpr int kB0 = (C + 1) & ~1;            // first batch start
+  static constexpr int kNBat = (kT - kB0 + 7) / 8;     // batches of step C
+};
+
+template <int C, int B>
+__device__ __forceinline__ void read_batch(double (&v)[8], const double* row) {
+  constexpr int m0 = StepShape<C>::kB0 + 8 * B;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
-    if (kB0 + t < kT) cur[t] = v[kB0 + t];
-#pragma unroll
-  for (int bi = 0; bi < kNBat; ++bi) {
-    const int mb = kB0 + 8 * bi;
-    if (bi + 1 < kNBat) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (mb + 8 + t < kT) nxt[t] = v[mb + 8 + t];
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      if (mb + t > C && mb + t < kT) a[mb + t] = __builtin_fma(-x, cur[t], a[mb + t]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
-  }
+    if (m0 + t < kT) v[t] = row[m0 + t];
 }
 
-// Branch-free steps (one basic block, so that no multiply-add is sunk into a
-// later step with its operand held live); a non-positive pivot is replaced
-// by 1 and counted in bad.
-template <int C>
-__device__ __forceinline__ void potrf_steps(double (&a)[kT], int r, double* col, int& bad) {
-  if constexpr (C < kT) {
-    double d = readlane_f64(a[C], C);
+template <int C, int B>
+__device__ __forceinline__ void fma_batch(double (&a)[kT], double x, const double (&v)[8]) {
+  constexpr int m0 = StepShape<C>::kB0 + 8 * B;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if (m0 + t > C && m0 + t < kT) a[m0 + t] = __builtin_fma(-x, v[t], a[m0 + t]);
+}
+
+// the next pivot's chain, stage S, for column C1 (1 / sqrt(d) from the
+// hardware estimate and two Newton steps, then the scaled column into LDS)
+struct PivotChain {
+  double d, y, h, t;
+  int bad;
+};
+template <int C1, int S>
+__device__ __forceinline__ void pivot_stage(double (&a)[kT], int r, double* col, PivotChain& pc) {
+  if constexpr (S == 0) {
+    const double d = readlane_f64(a[C1], C1);
     const bool ok = d > 0.0;  // d is the same in every lane
-    bad |= ok ? 0 : 1;
-    d = ok ? d : 1.0;
-    const double rp = rsqrt_f64(d);
-    // rows r >= C: the factor's entry (d rp on the diagonal); rows r < C
+    pc.bad |= ok ? 0 : 1;
+    pc.d = ok ? d : 1.0;
+  } else if constexpr (S == 1) {
+    pc.y = __builtin_amdgcn_rsq(pc.d);
+    pc.h = 0.5 * pc.d;
+  } else if constexpr (S == 2 || S == 5) {
+    pc.t = pc.h * -pc.y;
+  } else if constexpr (S == 3 || S == 6) {
+    pc.t = __builtin_fma(pc.t, pc.y, 1.5);
+  } else if constexpr (S == 4 || S == 7) {
+    pc.y = pc.y * pc.t;
+  } else if constexpr (S == 8) {
+    // rows r >= C1: the factor's entry (d rp on the diagonal); rows r < C1
     // hold entries above their diagonal here, which are never read
-    const double l = a[C] * rp;
-    a[C] = l;
-    // column C through LDS; the opaque offset keeps this step's reads after
-    // its own write
-    int off = 0;
-    asm volatile("" : "+v"(off));
-    double* cp = col + off;
-    cp[r] = l;
-    __builtin_amdgcn_wave_barrier();
-    // rows r < k receive updates of entries above their diagonal, which are
-    // never read: no per-lane condition
-    axpy_tail<C>(a, l, cp);
-    __builtin_amdgcn_wave_barrier();
-    potrf_steps<C + 1>(a, r, col, bad);
+    const double l = a[C1] * pc.y;
+    a[C1] = l;
+    col[r] = l;
+  }
+}
+constexpr int kPivotStages = 9;
+
+template <int C1, int S0, int S1>
+__device__ __forceinline__ void pivot_stages(double (&a)[kT], int r, double* col,
+                                             PivotChain& pc) {
+  if constexpr (S0 < S1 && S0 < kPivotStages) {
+    pivot_stage<C1, S0>(a, r, col, pc);
+    pivot_stages<C1, S0 + 1, S1>(a, r, col, pc);
   }
 }
 
-template <int C>
-__device__ __forceinline__ void trsm_steps(double (&a)[kT], const double* lt, const double* rd) {
-  if constexpr (C < kT) {
-    const double x = a[C] * rd[C];
-    a[C] = x;
-    // the row offset is made to depend on x, so that this step's reads are
-    // not hoisted ahead of the steps before it
-    int off = C * kTP;
-    asm volatile("" : "+v"(off) : "v"(x));
-    axpy_tail<C>(a, x, lt + off);
-    trsm_steps<C + 1>(a, lt, rd);
+// Factor: step C, batch B; cur holds the reads of (C, B) from colC (column C,
+// already scaled, in LDS); colN is the other buffer, for column C + 1.
+template <int C, int B>
+__device__ __forceinline__ void potrf_run(double (&a)[kT], int r, double* colC, double* colN,
+                                          double (&cur)[8], double l, PivotChain& pc) {
+  if constexpr (C < kT - 1) {
+    constexpr int nb = StepShape<C>::kNBat;
+    double nxt[8];
+    if constexpr (B + 1 < nb) read_batch<C, B + 1>(nxt, colC);
+    fma_batch<C, B>(a, l, cur);
+    // two chain stages per later batch (the first batch finished column C+1)
+    if constexpr (B >= 1) pivot_stages<C + 1, 2 * (B - 1), 2 * (B - 1) + 2>(a, r, colN, pc);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (B + 1 < nb) {
+      potrf_run<C, B + 1>(a, r, colC, colN, nxt, l, pc);
+    } else {
+      // finish the chain, then start step C + 1 from colN
+      if constexpr (B == 0)
+        pivot_stages<C + 1, 0, kPivotStages>(a, r, colN, pc);
+      else
+        pivot_stages<C + 1, 2 * B, kPivotStages>(a, r, colN, pc);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (C + 1 < kT - 1) {
+        double first[8];
+        read_batch<C + 1, 0>(first, colN);
+        potrf_run<C + 1, 0>(a, r, colN, colC, first, a[C + 1], pc);
+      }
+    }
+  }
+}
+
+// Solve: step C, batch B; cur holds the reads of (C, B) from row C of lt
+// (column C of the factor); x = a[C] / L[C][C].
+template <int C, int B>
+__device__ __forceinline__ void trsm_run(double (&a)[kT], const double* lt, const double* rd,
+                                         double (&cur)[8], double x) {
+  if constexpr (C < kT - 1) {
+    constexpr int nb = StepShape<C>::kNBat;
+    double nxt[8];
+    double rn = 0.0;
+    if constexpr (B + 1 < nb) {
+      read_batch<C, B + 1>(nxt, lt + C * kTP);
+    } else if constexpr (C + 1 < kT - 1) {
+      read_batch<C + 1, 0>(nxt, lt + (C + 1) * kTP);
+      rn = rd[C + 1];
+    } else {
+      rn = rd[C + 1];
+    }
+    fma_batch<C, B>(a, x, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (B + 1 < nb) {
+      trsm_run<C, B + 1>(a, lt, rd, nxt, x);
+    } else {
+      const double xn = a[C + 1] * rn;
+      a[C + 1] = xn;
+      trsm_run<C + 1, 0>(a, lt, rd, nxt, xn);
+    }
   }
 }
 
@@ -398,9 +452,18 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
           const double2 w = *reinterpret_cast<const double2*>(&ta[r][c]);
           a[c] = w.x, a[c + 1] = w.y;
         }
-        int bad = 0;
-        potrf_steps<0>(a, r, rd, bad);
-        if (bad) atomicOr(status, 1);  // the same in every lane
+        // column 0 by the chain, then the pipelined steps (two LDS column
+        // buffers, rd and the first row of tb)
+        PivotChain pc;
+        pc.bad = 0;
+        double* col0 = rd;
+        double* col1 = &tb[0][0];
+        pivot_stages<0, 0, kPivotStages>(a, r, col0, pc);
+        __builtin_amdgcn_sched_barrier(0);
+        double first[8];
+        read_batch<0, 0>(first, col0);
+        potrf_run<0, 0>(a, r, col0, col1, first, a[0], pc);
+        if (pc.bad) atomicOr(status, 1);  // the same in every lane
 #pragma unroll
         for (int c = 0; c < kT; ++c) ta[r][c] = a[c];
       }
@@ -437,7 +500,11 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
           const double2 x2 = *reinterpret_cast<const double2*>(&tb[lane][c]);
           a[c] = x2.x, a[c + 1] = x2.y;
         }
-        trsm_steps<0>(a, &ta[0][0], rd);
+        const double x0 = a[0] * rd[0];
+        a[0] = x0;
+        double first[8];
+        read_batch<0, 0>(first, &ta[0][0]);
+        trsm_run<0, 0>(a, &ta[0][0], rd, first, x0);
 #pragma unroll
         for (int c = 0; c < kT; ++c) tb[lane][c] = a[c];
       }
@@ -509,7 +576,7 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
 }
 
 // Step 4.  Workgroup b owns rows r0 = RW b .. r0 + RW - 1 (lane = row; RW is
-// 32 when workgroups of 32 rows all fit on the CUs at once, else 64).
+// 32, 48 or 64: the fewest whose workgroups all fit on the CUs at once).
 // DT is the residual matrix transposed, DT[i][n] = d_i of row n, so that a
 // wave's loads of one column are contiguous.
 template <int RW>
@@ -519,19 +586,33 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
     int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
     uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
-  static_assert(RW == 32 || RW == 64, "16-row product tiles, one lane per row");
-  constexpr int NRT = RW / 16;               // 16-row product tiles
-  constexpr int CPW = NRT / 2;               // 16-column product tiles per wave
-  static_assert(NRT * 4 == (kRowThreads / 64) * CPW, "one wave per group of product tiles");
+  static_assert(RW == 32 || RW == 48 || RW == 64, "16-row product tiles, one lane per row");
+  static_assert(kRowThreads == 512, "the product tiles are laid out for eight waves");
+  constexpr int NRT = RW / 16;               // 16-row product tiles (times 4 column tiles)
+  constexpr int CPW = RW == 32 ? 1 : 2;      // most 16-column product tiles of one wave
   __shared__ double dsm[kChunk][RW];        // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][RW];            // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
   __shared__ double rdi[kNB];               // 1 / R[jb + a][jb + a]
   __shared__ uint16_t ws[RW][kNB + 2];      // the block's original weights
   __shared__ uint32_t qs[RW][kNB / 4];       // the block's codes, stored together
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ml = lane & 15, kl = lane >> 4;
-  const int mb = (wave % NRT) * 16, nbw = (wave / NRT) * 16 * CPW;
+  // Product tiles of wave w (wave w runs on SIMD w mod 4): rows mb .. mb + 15,
+  // ncw column tiles from nbw.  RW = 32 and 64: NRT row tiles times 4 column
+  // tiles spread evenly (one or two per wave).  RW = 48: 12 tiles, two for
+  // waves 0-3 and one for waves 4-7, so that every SIMD holds three.
+  int mb, nbw, ncw;
+  if constexpr (RW == 48) {
+    if (wave < 4) {
+      mb = (wave >> 1) * 16, nbw = (wave & 1) * 32, ncw = 2;
+    } else {
+      mb = 32, nbw = (wave - 4) * 16, ncw = 1;
+    }
+  } else {
+    mb = (wave % NRT) * 16, nbw = (wave / NRT) * 16 * CPW, ncw = CPW;
+  }
   const int r0 = blockIdx.x * RW;
   const int row = r0 + lane;
   const bool valid = lane < RW && row < N;
@@ -543,7 +624,7 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
     const int nb = min(kNB, K - jb);
     // contribution of the columns before the block, on the fp64 matrix
     // cores: wave w sums rows mb .. mb + 15 and block columns
-    // nbw .. nbw + 16 CPW - 1 as 16 x 16 tiles (lane layout as in step 1);
+    // nbw .. nbw + 16 ncw - 1 as 16 x 16 tiles (lane layout as in step 1);
     // two waves per SIMD keep the matrix pipe busier than one
     f64x4_t acc[CPW];
 #pragma unroll
@@ -580,22 +661,35 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
       }
       __syncthreads();
       if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
+      auto mma_chunk = [&](auto nc) {
+        constexpr int NC = decltype(nc)::value;
 #pragma unroll
-      for (int kk = 0; kk < kChunk / 4; ++kk) {
-        const int ii = 4 * kk + kl;
-        const double a = dsm[ii][mb + ml];
-        double b[CPW];
+        for (int kk = 0; kk < kChunk / 4; ++kk) {
+          const int ii = 4 * kk + kl;
+          const double a = dsm[ii][mb + ml];
+          double b[NC];
 #pragma unroll
-        for (int v = 0; v < CPW; ++v) b[v] = rs[ii][nbw + 16 * v + ml];
+          for (int v = 0; v < NC; ++v) b[v] = rs[ii][nbw + 16 * v + ml];
 #pragma unroll
-        for (int v = 0; v < CPW; ++v)
-          acc[v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[v], acc[v], 0, 0, 0);
+          for (int v = 0; v < NC; ++v)
+            acc[v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[v], acc[v], 0, 0, 0);
+        }
+      };
+      if constexpr (CPW == 1) {
+        mma_chunk(std::integral_constant<int, 1>{});
+      } else {
+        if (ncw == 2)
+          mma_chunk(std::integral_constant<int, 2>{});
+        else
+          mma_chunk(std::integral_constant<int, 1>{});
       }
     }
 #pragma unroll
     for (int v = 0; v < CPW; ++v)
+      if (v < ncw) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + kl + 4 * e] = acc[v][e];
+        for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + kl + 4 * e] = acc[v][e];
+      }
     for (int e = tid; e < kNB * kNB; e += kRowThreads) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
@@ -757,14 +851,18 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
                      nt, chol_task_count(nt), ver, ticket, status);
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
-  // Rows per workgroup: 32 when those workgroups all run at once (one per
-  // CU), so that short layers spread over more CUs (the product part halves;
-  // the column walk does not change); else 64 (48 measured no faster on the
-  // 11008-row layer than 64).
+  // Rows per workgroup: the fewest of 32, 48 and 64 whose workgroups all
+  // run at once (one per CU), so that a layer spreads over as many CUs as it
+  // can (the product part shrinks with the rows; the column walk does not
+  // change); 64 for taller layers.
   const int qmax = (1 << bits) - 1, qlo = sym ? 1 : 0;
-  if ((n + 31) / 32 <= device_cu_count())
+  const int cus = device_cu_count();
+  if ((n + 31) / 32 <= cus)
     hipLaunchKernelGGL(gptq_rows_kernel<32>, dim3((n + 31) / 32), dim3(kRowThreads), 0, stream, w, n, k, A,
                        scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
+  else if ((n + 47) / 48 <= cus)
+    hipLaunchKernelGGL(gptq_rows_kernel<48>, dim3((n + 47) / 48), dim3(kRowThreads), 0, stream, w,
+                       n, k, A, scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
   else
     hipLaunchKernelGGL(gptq_rows_kernel<kRows>, dim3((n + kRows - 1) / kRows), dim3(kRowThreads), 0,
                        stream, w, n, k, A, scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
