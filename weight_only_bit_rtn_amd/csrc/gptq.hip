@@ -207,139 +207,96 @@ int chol_task_count(int nt) {
   return n;
 }
 
-// The factor and solve tasks run one wave over the 64 rows of a tile (lane r
-// holding row r in registers).  Step C updates the entries m > C of every
-// row with column C: a[m] -= x a_C[m], the a_C[m] read from LDS (broadcast)
-// in batches of eight.  Both are software-pipelined by hand: the reads of
-// the next batch (across step boundaries) go out before the multiply-adds of
-// this one, and in the factorization the next pivot's dependent chain
-// (pivot, reciprocal square root, scaling, LDS write) is spread over the
-// batches of the current step, whose first batch already finishes column
-// C + 1.  Scheduling barriers keep that order (left to itself, at the
-// register limit the compiler hoists every read and parks them in scratch).
-// Plain double reads, which the compiler pairs, keep their order with the
-// LDS stores to the same buffer.
-template <int C>
-struct StepShape {
-  static constexpr int kB0 = (C + 1) & ~1;            // first batch start
-  static constexpr int kNBat = (kT - kB0 + 7) / 8;     // batches of step C
-};
+// The factor and solve tasks work in panels of kP columns.  For a panel,
+// one wave (lane r holding row r's kP panel entries in registers) runs the
+// panel's column steps, each touching only the panel's own columns; then the
+// four waves apply the panel to the columns right of it as 16 x 16 tiles on
+// the fp64 matrix cores.  The serial chain per column is thus short (at most
+// kP - 1 multiply-adds), and the bulk of the work is matrix-core work.
+constexpr int kP = 16;
 
-template <int C, int B>
-__device__ __forceinline__ void read_batch(double (&v)[8], const double* row) {
-  constexpr int m0 = StepShape<C>::kB0 + 8 * B;
+// D[16 ti + m][16 tj + n] -= sum_{c < kP} P(16 ti + m, c0 + c) Q(16 tj + n, c0 + c),
+// m, n < 16, with P(r, c) = p[r pr + c pc] and Q(s, c) = q[s qr + c qc] in LDS;
+// D row-major with stride ldd.  Lane layout of v_mfma_f64_16x16x4f64 as in
+// the Hessian (lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and
+// holds D[l / 16 + 4 e][l % 16] in element e).
+__device__ __forceinline__ void tile_sub_product(double* d, int ldd, const double* p, int pr,
+                                                 int pc, const double* q, int qr, int qc, int ti,
+                                                 int tj, int c0, int lane) {
+  const int ml = lane & 15, kl = lane >> 4;
+  f64x4_t acc;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-    if (m0 + t < kT) v[t] = row[m0 + t];
+  for (int e = 0; e < 4; ++e) acc[e] = d[(16 * ti + kl + 4 * e) * ldd + 16 * tj + ml];
+#pragma unroll
+  for (int kk = 0; kk < kP / 4; ++kk) {
+    const int c = c0 + 4 * kk + kl;
+    const double av = -p[(16 * ti + ml) * pr + c * pc];
+    const double bv = q[(16 * tj + ml) * qr + c * qc];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d[(16 * ti + kl + 4 * e) * ldd + 16 * tj + ml] = acc[e];
 }
 
-template <int C, int B>
-__device__ __forceinline__ void fma_batch(double (&a)[kT], double x, const double (&v)[8]) {
-  constexpr int m0 = StepShape<C>::kB0 + 8 * B;
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    if (m0 + t > C && m0 + t < kT) a[m0 + t] = __builtin_fma(-x, v[t], a[m0 + t]);
+// 1 / sqrt(d) to fp64 accuracy: the hardware estimate and two Newton steps
+__device__ __forceinline__ double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  y = y * (1.5 - 0.5 * d * y * y);
+  y = y * (1.5 - 0.5 * d * y * y);
+  return y;
 }
 
-// the next pivot's chain, stage S, for column C1 (1 / sqrt(d) from the
-// hardware estimate and two Newton steps, then the scaled column into LDS)
-struct PivotChain {
-  double d, y, h, t;
-  int bad;
-};
-template <int C1, int S>
-__device__ __forceinline__ void pivot_stage(double (&a)[kT], int r, double* col, PivotChain& pc) {
-  if constexpr (S == 0) {
-    const double d = readlane_f64(a[C1], C1);
+// Factor panel C0 of an LDS tile t (row stride kTP, lower triangle valid,
+// earlier panels already applied): one wave, lane r = row r.  Column C0 + c
+// goes to every lane through one of two LDS column buffers.  Branch-free (a
+// non-positive pivot is replaced by 1 and counted in bad).
+template <int C0>
+__device__ __forceinline__ void potrf_panel(double* t, int r, double* colA, double* colB,
+                                            int& bad) {
+  double a[kP];
+#pragma unroll
+  for (int c = 0; c < kP; ++c) a[c] = t[r * kTP + C0 + c];
+#pragma unroll
+  for (int c = 0; c < kP; ++c) {
+    double d = readlane_f64(a[c], C0 + c);
     const bool ok = d > 0.0;  // d is the same in every lane
-    pc.bad |= ok ? 0 : 1;
-    pc.d = ok ? d : 1.0;
-  } else if constexpr (S == 1) {
-    pc.y = __builtin_amdgcn_rsq(pc.d);
-    pc.h = 0.5 * pc.d;
-  } else if constexpr (S == 2 || S == 5) {
-    pc.t = pc.h * -pc.y;
-  } else if constexpr (S == 3 || S == 6) {
-    pc.t = __builtin_fma(pc.t, pc.y, 1.5);
-  } else if constexpr (S == 4 || S == 7) {
-    pc.y = pc.y * pc.t;
-  } else if constexpr (S == 8) {
-    // rows r >= C1: the factor's entry (d rp on the diagonal); rows r < C1
-    // hold entries above their diagonal here, which are never read
-    const double l = a[C1] * pc.y;
-    a[C1] = l;
+    bad |= ok ? 0 : 1;
+    d = ok ? d : 1.0;
+    // rows r >= C0 + c: the factor's entry (d rp on the diagonal); rows
+    // above hold entries right of their diagonal here, which are never read
+    const double l = a[c] * rsqrt_f64(d);
+    a[c] = l;
+    double* col = (c & 1) ? colB : colA;
     col[r] = l;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = c + 1; m < kP; ++m) a[m] = __builtin_fma(-l, col[C0 + m], a[m]);
   }
-}
-constexpr int kPivotStages = 9;
-
-template <int C1, int S0, int S1>
-__device__ __forceinline__ void pivot_stages(double (&a)[kT], int r, double* col,
-                                             PivotChain& pc) {
-  if constexpr (S0 < S1 && S0 < kPivotStages) {
-    pivot_stage<C1, S0>(a, r, col, pc);
-    pivot_stages<C1, S0 + 1, S1>(a, r, col, pc);
-  }
+#pragma unroll
+  for (int c = 0; c < kP; ++c) t[r * kTP + C0 + c] = a[c];
 }
 
-// Factor: step C, batch B; cur holds the reads of (C, B) from colC (column C,
-// already scaled, in LDS); colN is the other buffer, for column C + 1.
-template <int C, int B>
-__device__ __forceinline__ void potrf_run(double (&a)[kT], int r, double* colC, double* colN,
-                                          double (&cur)[8], double l, PivotChain& pc) {
-  if constexpr (C < kT - 1) {
-    constexpr int nb = StepShape<C>::kNBat;
-    double nxt[8];
-    if constexpr (B + 1 < nb) read_batch<C, B + 1>(nxt, colC);
-    fma_batch<C, B>(a, l, cur);
-    // two chain stages per later batch (the first batch finished column C+1)
-    if constexpr (B >= 1) pivot_stages<C + 1, 2 * (B - 1), 2 * (B - 1) + 2>(a, r, colN, pc);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (B + 1 < nb) {
-      potrf_run<C, B + 1>(a, r, colC, colN, nxt, l, pc);
-    } else {
-      // finish the chain, then start step C + 1 from colN
-      if constexpr (B == 0)
-        pivot_stages<C + 1, 0, kPivotStages>(a, r, colN, pc);
-      else
-        pivot_stages<C + 1, 2 * B, kPivotStages>(a, r, colN, pc);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (C + 1 < kT - 1) {
-        double first[8];
-        read_batch<C + 1, 0>(first, colN);
-        potrf_run<C + 1, 0>(a, r, colN, colC, first, a[C + 1], pc);
-      }
-    }
+// Solve panel C0 of the rows x (LDS, row stride kTP) against the factor,
+// lt[c][m] = L[m][c] (column c of the factor as an LDS row), rd[c] =
+// 1 / L[c][c]: one wave, lane r = row r.
+template <int C0>
+__device__ __forceinline__ void trsm_panel(double* x, int r, const double* lt, const double* rd) {
+  double a[kP];
+#pragma unroll
+  for (int c = 0; c < kP; ++c) a[c] = x[r * kTP + C0 + c];
+#pragma unroll
+  for (int c = 0; c < kP; ++c) {
+    const double xc = a[c] * rd[C0 + c];
+    a[c] = xc;
+    // the factor row's offset depends on xc, so that the compiler does not
+    // hoist every step's reads to the start
+    int off = (C0 + c) * kTP;
+    asm volatile("" : "+v"(off) : "v"(xc));
+#pragma unroll
+    for (int m = c + 1; m < kP; ++m) a[m] = __builtin_fma(-xc, lt[off + C0 + m], a[m]);
   }
-}
-
-// Solve: step C, batch B; cur holds the reads of (C, B) from row C of lt
-// (column C of the factor); x = a[C] / L[C][C].
-template <int C, int B>
-__device__ __forceinline__ void trsm_run(double (&a)[kT], const double* lt, const double* rd,
-                                         double (&cur)[8], double x) {
-  if constexpr (C < kT - 1) {
-    constexpr int nb = StepShape<C>::kNBat;
-    double nxt[8];
-    double rn = 0.0;
-    if constexpr (B + 1 < nb) {
-      read_batch<C, B + 1>(nxt, lt + C * kTP);
-    } else if constexpr (C + 1 < kT - 1) {
-      read_batch<C + 1, 0>(nxt, lt + (C + 1) * kTP);
-      rn = rd[C + 1];
-    } else {
-      rn = rd[C + 1];
-    }
-    fma_batch<C, B>(a, x, cur);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (B + 1 < nb) {
-      trsm_run<C, B + 1>(a, lt, rd, nxt, x);
-    } else {
-      const double xn = a[C + 1] * rn;
-      a[C + 1] = xn;
-      trsm_run<C + 1, 0>(a, lt, rd, nxt, xn);
-    }
-  }
+#pragma unroll
+  for (int c = 0; c < kP; ++c) x[r * kTP + C0 + c] = a[c];
 }
 
 __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__ A, int K, int nt,
@@ -444,29 +401,30 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
         ta[r][ec] = (r < nbi && ec <= r) ? v[q] : (r == ec ? 1.0 : 0.0);
       }
       __syncthreads();
-      if (wave == 0) {
-        const int r = lane;
-        double a[kT];
-#pragma unroll
-        for (int c = 0; c < kT; c += 2) {
-          const double2 w = *reinterpret_cast<const double2*>(&ta[r][c]);
-          a[c] = w.x, a[c + 1] = w.y;
+      // panels of kP columns: the panel's column steps on one wave, then the
+      // lower tiles right of and below the panel updated on the matrix cores
+      int bad = 0;
+      auto panel = [&](auto c0v) {
+        constexpr int C0 = decltype(c0v)::value;
+        if (wave == 0) potrf_panel<C0>(&ta[0][0], lane, rd, &tb[0][0], bad);
+        __syncthreads();
+        if constexpr (C0 + kP < kT) {
+          constexpr int n = (kT - C0 - kP) / 16, p0 = (C0 + kP) / 16;
+          for (int t = wave; t < n * (n + 1) / 2; t += 4) {
+            int ti = 0;
+            while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+            const int tj = t - ti * (ti + 1) / 2;
+            tile_sub_product(&ta[0][0], kTP, &ta[0][0], kTP, 1, &ta[0][0], kTP, 1, p0 + ti, p0 + tj,
+                             C0, lane);
+          }
+          __syncthreads();
         }
-        // column 0 by the chain, then the pipelined steps (two LDS column
-        // buffers, rd and the first row of tb)
-        PivotChain pc;
-        pc.bad = 0;
-        double* col0 = rd;
-        double* col1 = &tb[0][0];
-        pivot_stages<0, 0, kPivotStages>(a, r, col0, pc);
-        __builtin_amdgcn_sched_barrier(0);
-        double first[8];
-        read_batch<0, 0>(first, col0);
-        potrf_run<0, 0>(a, r, col0, col1, first, a[0], pc);
-        if (pc.bad) atomicOr(status, 1);  // the same in every lane
-#pragma unroll
-        for (int c = 0; c < kT; ++c) ta[r][c] = a[c];
-      }
+      };
+      panel(std::integral_constant<int, 0>{});
+      panel(std::integral_constant<int, 16>{});
+      panel(std::integral_constant<int, 32>{});
+      panel(std::integral_constant<int, 48>{});
+      if (wave == 0 && bad) atomicOr(status, 1);  // the same in every lane
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -493,21 +451,24 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
       }
       if (tid < kT) rd[tid] = 1.0 / dg;
       __syncthreads();
-      if (wave == 0) {
-        double a[kT];
-#pragma unroll
-        for (int c = 0; c < kT; c += 2) {
-          const double2 x2 = *reinterpret_cast<const double2*>(&tb[lane][c]);
-          a[c] = x2.x, a[c + 1] = x2.y;
+      // panels of kP columns: the panel's column steps on one wave, then the
+      // columns right of the panel, all rows, updated on the matrix cores
+      auto panel = [&](auto c0v) {
+        constexpr int C0 = decltype(c0v)::value;
+        if (wave == 0) trsm_panel<C0>(&tb[0][0], lane, &ta[0][0], rd);
+        __syncthreads();
+        if constexpr (C0 + kP < kT) {
+          constexpr int n = (kT - C0 - kP) / 16, p0 = (C0 + kP) / 16;
+          for (int t = wave; t < 4 * n; t += 4)
+            tile_sub_product(&tb[0][0], kTP, &tb[0][0], kTP, 1, &ta[0][0], 1, kTP, t & 3,
+                             p0 + (t >> 2), C0, lane);
+          __syncthreads();
         }
-        const double x0 = a[0] * rd[0];
-        a[0] = x0;
-        double first[8];
-        read_batch<0, 0>(first, &ta[0][0]);
-        trsm_run<0, 0>(a, &ta[0][0], rd, first, x0);
-#pragma unroll
-        for (int c = 0; c < kT; ++c) tb[lane][c] = a[c];
-      }
+      };
+      panel(std::integral_constant<int, 0>{});
+      panel(std::integral_constant<int, 16>{});
+      panel(std::integral_constant<int, 32>{});
+      panel(std::integral_constant<int, 48>{});
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
