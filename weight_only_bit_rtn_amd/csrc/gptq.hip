@@ -663,54 +663,103 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
       ws[rr][c] = (r0 + rr < N && c < nb) ? w[(int64_t)(r0 + rr) * K + jb + c] : (uint16_t)0;
     }
     __syncthreads();
-    // the block's columns in order, one lane per row; the row's running
-    // sums for the block's columns stay in registers
-    if (wave == 0) {
-      // a 64-column block meets at most two groups (groups are multiples of
-      // 32 columns, blocks start on multiples of 64)
-      const int g0 = jb / gsz, g1 = min((jb + nb - 1) / gsz, G - 1);
+    // The block's columns in order, one lane per row, the row's running sums
+    // in registers, in two halves of kNB / 2 columns: a column's decision
+    // updates only the sums of its own half, and between the halves the
+    // first half's residuals enter the second half's sums as one small
+    // product on the matrix cores (the serial chain per column then carries
+    // at most kNB / 2 - 1 multiply-adds instead of kNB - 1).
+    constexpr int kH = kNB / 2;
+    // a 64-column block meets at most two groups (groups are multiples of
+    // 32 columns, blocks start on multiples of 64)
+    const int g0 = jb / gsz, g1 = min((jb + nb - 1) / gsz, G - 1);
+    // column j's decision for the lane's row from its running sum: code into
+    // qs, residual into DT (and returned)
+    auto decide = [&](int j, double cbj, double s0, double s1, int64_t z0, int64_t z1) {
+      const int col = jb + j;
+      const bool first = col / gsz == g0;
+      const double s = first ? s0 : s1;
+      const int64_t z = first ? z0 : z1;
+      const double wv = h_bits_to_f64(ws[lr][j]);
+      const double t = wv + cbj * rdi[j];
+      int64_t q = (int64_t)__builtin_rint(t / s) + z;
+      q = q < qlo ? qlo : (q > M ? M : q);
+      // the dequantized weight (q - z) * s, exact in fp64
+      const double deq = (double)(q - z) * s;
+      const double d = wv - deq;
+      if (lane < RW) reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
+      if (valid) DT[(int64_t)col * N + row] = d;
+      return d;
+    };
+    // the half [J0, J0 + kH): running sums cbh, factor rows of the block in
+    // 16-byte reads, four entries at a time, issued before their
+    // multiply-adds; the residuals go to dh (when given)
+    auto walk_half = [&](auto j0v, double (&cbh)[kH], double* dh) {
+      constexpr int J0 = decltype(j0v)::value;
       const double s0 = valid ? h_bits_to_f64(scales[(int64_t)row * G + g0]) : 1.0;
       const double s1 = valid ? h_bits_to_f64(scales[(int64_t)row * G + g1]) : 1.0;
       const int64_t z0 = valid ? zeros[(int64_t)row * G + g0] : 0;
       const int64_t z1 = valid ? zeros[(int64_t)row * G + g1] : 0;
-      double cb[kNB];
 #pragma unroll
-      for (int j = 0; j < kNB; ++j) cb[j] = cs[j][lr];
-#pragma unroll
-      for (int j = 0; j < kNB; ++j) {
+      for (int jj = 0; jj < kH; ++jj) {
+        const int j = J0 + jj;
         if (j < nb) {
-          const int col = jb + j;
-          const bool first = col / gsz == g0;
-          const double s = first ? s0 : s1;
-          const int64_t z = first ? z0 : z1;
-          const double wv = h_bits_to_f64(ws[lr][j]);
-          const double t = wv + cb[j] * rdi[j];
-          int64_t q = (int64_t)__builtin_rint(t / s) + z;
-          q = q < qlo ? qlo : (q > M ? M : q);
-          // the dequantized weight (q - z) * s, exact in fp64
-          const double deq = (double)(q - z) * s;
-          const double d = wv - deq;
-          if (lane < RW) reinterpret_cast<uint8_t*>(qs[lane])[j] = (uint8_t)q;
-          if (valid) DT[(int64_t)col * N + row] = d;
-          // row j of the block's factor in 16-byte reads, four entries at a
-          // time, issued before their multiply-adds
+          const double d = decide(j, cbh[jj], s0, s1, z0, z1);
+          if (dh) dh[jj] = d;
 #pragma unroll
-          for (int j2b = (j + 1) & ~1; j2b < kNB; j2b += 4) {
+          for (int j2b = (jj + 1) & ~1; j2b < kH; j2b += 4) {
             double r8[4];
 #pragma unroll
             for (int t = 0; t < 4; t += 2) {
-              if (j2b + t < kNB) {
-                const double2 v = *reinterpret_cast<const double2*>(&rb[j][j2b + t]);
+              if (j2b + t < kH) {
+                const double2 v = *reinterpret_cast<const double2*>(&rb[j][J0 + j2b + t]);
                 r8[t] = v.x, r8[t + 1] = v.y;
               }
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int j2 = j2b + t;
-              if (j2 > j && j2 < kNB) cb[j2] = __builtin_fma(d, r8[t], cb[j2]);
+              if (j2 > jj && j2 < kH) cbh[j2] = __builtin_fma(d, r8[t], cbh[j2]);
             }
           }
         }
+      }
+    };
+    if (wave == 0) {
+      double cbh[kH], dh[kH];
+#pragma unroll
+      for (int jj = 0; jj < kH; ++jj) cbh[jj] = cs[jj][lr];
+      walk_half(std::integral_constant<int, 0>{}, cbh, dh);
+      // the first half's residuals for the cross product (dsm is free now)
+      if (lane < RW) {
+#pragma unroll
+        for (int jj = 0; jj < kH; ++jj) dsm[jj][lane] = dh[jj];
+      }
+    }
+    __syncthreads();
+    if (nb > kH) {
+      // second-half sums += (first-half residuals) x (factor rows 0..kH-1,
+      // columns kH..kNB-1): NRT x 2 tiles of 16 x 16, one per wave
+      if (wave < 2 * NRT) {
+        const int rt = wave % NRT, ct = 2 + wave / NRT;
+        f64x4_t acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = cs[16 * ct + ml][16 * rt + kl + 4 * e];
+#pragma unroll
+        for (int kk = 0; kk < kH / 4; ++kk) {
+          const int jj = 4 * kk + kl;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(dsm[jj][16 * rt + ml], rb[jj][16 * ct + ml],
+                                                     acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[16 * ct + ml][16 * rt + kl + 4 * e] = acc[e];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        double cbh[kH];
+#pragma unroll
+        for (int jj = 0; jj < kH; ++jj) cbh[jj] = cs[kH + jj][lr];
+        walk_half(std::integral_constant<int, kH>{}, cbh, nullptr);
       }
     }
     __syncthreads();
