@@ -6,7 +6,7 @@ code in fp64; they compute the running weights in different (algebraically
 equal) ways, so a code could differ only where a quotient falls within about
 1e-12 of a rounding midpoint, which seeded continuous inputs do not produce.
 Shapes cover K that is not a multiple of the 64-column block, ragged row
-tiles (32-, 48- and 64-row workgroups), every width, per-row and grouped grids (power-of-two and other group
+tiles (16-, 32-, 48- and 64-row workgroups), every width, per-row and grouped grids (power-of-two and other group
 sizes), and one workload layer at full size (every row through the oracle).
 """
 from __future__ import annotations
@@ -74,14 +74,15 @@ def _check(lw, w, x, bits, g, damp, what, codes=True, packed=True, symmetric=Fal
     return rc
 
 
-# The row kernel takes the fewest of 32, 48 and 64 rows per workgroup whose
-# workgroups all fit on the CUs at once (256 on MI355X): the 8200-row shapes
-# take the 48-row form (ragged: 8200 = 170 * 48 + 40), the 16448-row shapes
-# the 64-row form, all others the 32-row form.
+# The row kernel takes the fewest of 16, 32, 48 and 64 rows per workgroup
+# whose workgroups all fit on the CUs at once (256 on MI355X): the 4100-row
+# shape takes the 32-row form (4100 = 128 * 32 + 4), the 8200-row shapes the
+# 48-row form (8200 = 170 * 48 + 40), the 16448-row shapes the 64-row form,
+# all others the 16-row form.
 CASES = [(5, 32, 4, 0), (17, 128, 3, 0), (64, 192, 2, 32), (67, 128, 4, 64), (130, 96, 8, 0),
          (70, 160, 4, 32), (33, 352, 4, 0), (129, 512, 3, 128), (40, 480, 4, 96),
-         (21, 320, 2, 64), (66, 256, 8, 32), (8200, 96, 4, 32), (8200, 320, 2, 0), (16448, 128, 3, 0),
-         (16448, 224, 4, 32)]
+         (21, 320, 2, 64), (66, 256, 8, 32), (4100, 128, 3, 32), (8200, 96, 4, 32), (8200, 320, 2, 0),
+         (16448, 128, 3, 0), (16448, 224, 4, 32)]
 
 
 @pytest.mark.parametrize("N,K,bits,g", CASES)

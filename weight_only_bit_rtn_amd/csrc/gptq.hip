@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256, 2) void chol_tiles_kernel(double* __restrict__
 }
 
 // Step 4.  Workgroup b owns rows r0 = RW b .. r0 + RW - 1 (lane = row; RW is
-// 32, 48 or 64: the fewest whose workgroups all fit on the CUs at once).
+// 16, 32, 48 or 64: the fewest whose workgroups all fit on the CUs at once).
 // DT is the residual matrix transposed, DT[i][n] = d_i of row n, so that a
 // wave's loads of one column are contiguous.
 template <int RW>
@@ -547,10 +547,10 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
     int M, int qlo /* lowest code: 0, or 1 on the symmetric grid */, double* __restrict__ DT,
     uint8_t* __restrict__ codes) {
   __shared__ double rs[kChunk][kNB];        // R[i0 + ii][jb + c], earlier columns
-  static_assert(RW == 32 || RW == 48 || RW == 64, "16-row product tiles, one lane per row");
+  static_assert(RW == 16 || RW == 32 || RW == 48 || RW == 64, "16-row tiles, one lane per row");
   static_assert(kRowThreads == 512, "the product tiles are laid out for eight waves");
   constexpr int NRT = RW / 16;               // 16-row product tiles (times 4 column tiles)
-  constexpr int CPW = RW == 32 ? 1 : 2;      // most 16-column product tiles of one wave
+  constexpr int CPW = RW <= 32 ? 1 : 2;      // most 16-column product tiles of one wave
   __shared__ double dsm[kChunk][RW];        // DT[i0 + ii][r0 + lane], their residuals
   __shared__ double cs[kNB][RW];            // sum_{i < j} d_i R_ij of each (column, row)
   __shared__ double rb[kNB][kNB + 2];       // R[jb + a][jb + c], the block's own rows (16-byte rows)
@@ -563,9 +563,13 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
   // Product tiles of wave w (wave w runs on SIMD w mod 4): rows mb .. mb + 15,
   // ncw column tiles from nbw.  RW = 32 and 64: NRT row tiles times 4 column
   // tiles spread evenly (one or two per wave).  RW = 48: 12 tiles, two for
-  // waves 0-3 and one for waves 4-7, so that every SIMD holds three.
-  int mb, nbw, ncw;
-  if constexpr (RW == 48) {
+  // waves 0-3 and one for waves 4-7, so that every SIMD holds three.  RW =
+  // 16: 4 tiles, each summed by two waves over the two halves of a chunk
+  // (kh), the halves added in LDS.
+  int mb, nbw, ncw, kh = 0;
+  if constexpr (RW == 16) {
+    mb = 0, nbw = (wave & 3) * 16, ncw = 1, kh = wave >> 2;
+  } else if constexpr (RW == 48) {
     if (wave < 4) {
       mb = (wave >> 1) * 16, nbw = (wave & 1) * 32, ncw = 2;
     } else {
@@ -624,9 +628,10 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
       if (ch + 1 < nchunks) fetch((ch + 1) * kChunk);
       auto mma_chunk = [&](auto nc) {
         constexpr int NC = decltype(nc)::value;
+        constexpr int NKK = RW == 16 ? kChunk / 8 : kChunk / 4;
 #pragma unroll
-        for (int kk = 0; kk < kChunk / 4; ++kk) {
-          const int ii = 4 * kk + kl;
+        for (int k2 = 0; k2 < NKK; ++k2) {
+          const int ii = 4 * (k2 + NKK * kh) + kl;
           const double a = dsm[ii][mb + ml];
           double b[NC];
 #pragma unroll
@@ -645,12 +650,25 @@ __global__ __launch_bounds__(kRowThreads) void gptq_rows_kernel(
           mma_chunk(std::integral_constant<int, 1>{});
       }
     }
+    if constexpr (RW == 16) {
+      // waves 4-7 hold the second halves of the chunks' sums
+      if (kh == 1) {
 #pragma unroll
-    for (int v = 0; v < CPW; ++v)
-      if (v < ncw) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + kl + 4 * e] = acc[v][e];
+        for (int e = 0; e < 4; ++e) cs[nbw + ml][kl + 4 * e] = acc[0][e];
       }
+      __syncthreads();
+      if (kh == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[nbw + ml][kl + 4 * e] += acc[0][e];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < CPW; ++v)
+        if (v < ncw) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cs[nbw + 16 * v + ml][mb + kl + 4 * e] = acc[v][e];
+        }
+    }
     for (int e = tid; e < kNB * kNB; e += kRowThreads) {
       const int a = e / kNB, c = e % kNB;
       rb[a][c] = (a < nb && c < nb && c >= a) ? Rat(jb + a, jb + c) : 0.0;
@@ -861,13 +879,16 @@ hipError_t launch_gptq(const uint16_t* w, int64_t N, int64_t K, const uint16_t* 
                      nt, chol_task_count(nt), ver, ticket, status);
   const int gsz = (int)(group_size == 0 ? K : group_size);
   const int G = (int)(K / gsz);
-  // Rows per workgroup: the fewest of 32, 48 and 64 whose workgroups all
+  // Rows per workgroup: the fewest of 16, 32, 48 and 64 whose workgroups all
   // run at once (one per CU), so that a layer spreads over as many CUs as it
   // can (the product part shrinks with the rows; the column walk does not
   // change); 64 for taller layers.
   const int qmax = (1 << bits) - 1, qlo = sym ? 1 : 0;
   const int cus = device_cu_count();
-  if ((n + 31) / 32 <= cus)
+  if ((n + 15) / 16 <= cus)
+    hipLaunchKernelGGL(gptq_rows_kernel<16>, dim3((n + 15) / 16), dim3(kRowThreads), 0, stream, w,
+                       n, k, A, scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
+  else if ((n + 31) / 32 <= cus)
     hipLaunchKernelGGL(gptq_rows_kernel<32>, dim3((n + 31) / 32), dim3(kRowThreads), 0, stream, w, n, k, A,
                        scales, zeros, G, gsz, qmax, qlo, DT, out_codes);
   else if ((n + 47) / 48 <= cus)
