@@ -177,3 +177,42 @@ def test_gptq_full_size(lw):
     assert np.array_equal(out["zeros"].cpu().numpy(), rz)
     want = harness.oracle.pack(rc, layer.bits)
     assert np.array_equal(out["packed"].cpu().numpy().view(np.uint32), want)
+
+
+def test_gptq_full_size_factor_11008x4096(lw):
+    """The 11008 x 4096, 2-bit, groups-of-64 layer with 4096 calibration rows
+    (the bench's size; the oracle's inverse-Hessian form is too slow here):
+    the GPU's own intermediate in the caller's workspace, the Cholesky factor
+    L of the index-reversed Hessian (64 x 64 tiles, 64 per side, in the
+    lower triangle at byte 256), against numpy in fp64: rows of L L^T equal
+    the same rows of reverse(H), H = (2/n) X^T X + damp mean(diag) I, on
+    sampled rows (tile edges, both ends, random ones) and on the whole
+    diagonal.  Also every code lies on the grid."""
+    import torch
+    N, K, bits, g, n, damp = 11008, 4096, 2, 64, 4096, 0.01
+    _say(f"[gptq factor] N={N} K={K} n={n}")
+    rng = np.random.default_rng(4096)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((n, K)).astype(np.float16)
+    need = lw.gptq_workspace_bytes(N, K)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda:0")
+    off = (-ws.data_ptr()) % 256
+    out = lw.quantize_gptq(_to_gpu(w), _to_gpu(x), bits, g, damp, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    A = ws[off + 256: off + 256 + K * K * 8].view(torch.float64).reshape(K, K).cpu().numpy()
+    L = np.tril(A)
+    x64 = x.astype(np.float64)
+    H = (2.0 / n) * (x64.T @ x64)
+    H += damp * np.mean(np.diag(H)) * np.eye(K)
+    R = H[::-1, ::-1]
+    rows = sorted(set([0, 1, 63, 64, 65, 127, 128, 2047, 2048, 4031, 4032, K - 2, K - 1]
+                      + rng.choice(K, 48, replace=False).tolist()))
+    scale = np.abs(np.diag(R)).max()
+    err = np.abs(L[rows] @ L.T - R[rows]).max() / scale
+    assert err < 1e-11, f"rows of L L^T differ from reverse(H) by {err:.3g} (relative)"
+    dg = np.einsum("ij,ij->i", L, L)
+    assert np.abs(dg - np.diag(R)).max() / scale < 1e-11
+    assert np.all(np.diag(L) > 0)
+    codes = out["codes"].cpu().numpy()
+    assert codes.max() <= (1 << bits) - 1
