@@ -85,7 +85,7 @@ __device__ __forceinline__ HalfParams params_at(const RowParams<META>& rp, int g
   return hp;
 }
 
-template <int BITS, int BT, int GM, bool META>
+template <int BITS, int BT, int GM, bool META, bool SS>
 __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     const uint16_t* __restrict__ x, int B, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros,
@@ -115,6 +115,17 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   // (batch tiles of 64 rows leave too little LDS, and the code would cost
   // them registers, so they never stage)
   constexpr bool kStage = GM == kWideGroups && BT <= 2;
+  // Batch tiles of 64 rows have no room for a round's copy; instead, in the
+  // SS variant (the host's choice: wide groups of exactly a run's span, K in
+  // whole steps, 16-byte aligned arrays, every round of every workgroup with
+  // at least five row groups, hence one K part), each step's parameters of
+  // all the round's rows are staged next to the step's activations, double
+  // buffered: one cooperative load per wave and step instead of two loads
+  // per lane.  Layout: 8 words per row, the scales (fp16 pairs) from word 0,
+  // the zeros (or compact words) from word 4.
+  static_assert(!SS || (GM == kWideGroups && BT == 4), "step staging: 64-row tiles, wide groups");
+  constexpr bool kStepStage = SS;
+  uint32_t* const ps = slow_scratch + kWaves * W * 64;
   const int ssw = G / 2 + 2, zsw = G + 4;
   const int pww = META ? 16 * zsw : 16 * (ssw + zsw);
 
@@ -243,6 +254,48 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     // as vectors (see load_w)
     constexpr int NVMAX = kRuns2 ? NWMAX / 2 : NWMAX;
     const bool wide_vec = NW == NWMAX && gsz == 4 * RN * U::CODES && G % NVMAX == 0;
+    // every wave of the round walks the same step (one K part): stage its
+    // parameters cooperatively (see kStepStage)
+    constexpr bool sstage = kStepStage;  // (one K part: the host's condition)
+    // Step t's parameters: waves 0-1 load the scales (compact words) of rows
+    // 64 w .. 64 w + 63 of the round, waves 2-3 the zeros, one 16-byte load
+    // per lane; every other wave, and every wave when staging is off, loads
+    // from an empty descriptor (zeros, no memory traffic), so each wave
+    // issues the same loads on every path.
+    const int prole = META ? (wave < 2 ? 0 : 2) : (wave < 4 ? wave >> 1 : 2);  // 0 s, 1 z, 2 none
+    const int prow = 64 * (wave & 1) + lane;
+    uint4 pr = make_uint4(0u, 0u, 0u, 0u);
+    auto fetch_p = [&](int t) {
+      const bool on = sstage && prole < 2 && prow < RG * 16;
+      const uint32_t esz = prole == 0 && !META ? 2u : 4u;
+      const void* base = prole == 0 ? static_cast<const void*>(scales)
+                                    : static_cast<const void*>(zeros);
+      const uint64_t bb = reinterpret_cast<uint64_t>(base);
+      const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+      const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+      const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(prole < 2 ? min((int64_t)N * G * esz, (int64_t)0x7fffffff) : 0));
+      const auto prs = make_rsrc(reinterpret_cast<const void*>(((uint64_t)bhi << 32) | blo), bytes);
+      const int64_t nr = min(16 * gr0 + prow, N - 1);
+      const uint32_t off = on ? (uint32_t)((nr * G + (int64_t)t * NVMAX) * esz) : 0u;
+      const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0);
+      pr = make_uint4(v.x, v.y, v.z, v.w);
+    };
+    auto store_p = [&](int buf) {
+      if (!(sstage && prole < 2 && prow < RG * 16)) return;
+      uint32_t* d = ps + buf * 1024 + 8 * prow;
+      if (prole == 0 && !META) {
+        d[0] = pr.x;
+        if constexpr (NVMAX == 4) d[1] = pr.y;
+      } else {
+        d[4] = pr.x;
+        d[5] = pr.y;
+        if constexpr (NVMAX == 4) {
+          d[6] = pr.z;
+          d[7] = pr.w;
+        }
+      }
+    };
     // index of the first unit of u's run (its group constants live there;
     // a compile-time index after unrolling)
     auto run_start = [](int u) { return kRuns2 ? (u & ~1) : u; };
@@ -288,66 +341,68 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
         }
       }
       if constexpr (GM == kWideGroups) {
-        // One group per run of units.  A full step (K split in one part)
-        // whose group size is exactly the unit span takes consecutive groups
-        // g0 .. g0 + NVMAX - 1 for its runs, g0 a multiple of NVMAX: one
-        // vector load per parameter array instead of one load per run
-        // (measured 5-10% faster at batches 16 and 32 on scale/zero arrays).
-        // Otherwise, and for the row's last step, the groups load per run.
-        const int g0 = min(my_unit(t, 0).ka, K - 1) >> gshift;
-        if (wide_vec && g0 + NVMAX <= G) {
-          uint16_t sv[NVMAX];
-          int32_t zv[NVMAX];
-          if (kStage && pstage) {
-            uint32_t wv[NVMAX];
-            if constexpr (META) {
-              const uint32_t* mp = pw + i16 * zsw + g0;
-              if constexpr (NVMAX == 4) {
-                const uint4 v = *reinterpret_cast<const uint4*>(mp);
-                wv[0] = v.x, wv[1] = v.y, wv[2] = v.z, wv[3] = v.w;
+        if constexpr (!sstage) {
+          // One group per run of units.  A full step (K split in one part)
+          // whose group size is exactly the unit span takes consecutive groups
+          // g0 .. g0 + NVMAX - 1 for its runs, g0 a multiple of NVMAX: one
+          // vector load per parameter array instead of one load per run
+          // (measured 5-10% faster at batches 16 and 32 on scale/zero arrays).
+          // Otherwise, and for the row's last step, the groups load per run.
+          const int g0 = min(my_unit(t, 0).ka, K - 1) >> gshift;
+          if (wide_vec && g0 + NVMAX <= G) {
+            uint16_t sv[NVMAX];
+            int32_t zv[NVMAX];
+            if (kStage && pstage) {
+              uint32_t wv[NVMAX];
+              if constexpr (META) {
+                const uint32_t* mp = pw + i16 * zsw + g0;
+                if constexpr (NVMAX == 4) {
+                  const uint4 v = *reinterpret_cast<const uint4*>(mp);
+                  wv[0] = v.x, wv[1] = v.y, wv[2] = v.z, wv[3] = v.w;
+                } else {
+                  const uint2 v = *reinterpret_cast<const uint2*>(mp);
+                  wv[0] = v.x, wv[1] = v.y;
+                }
+#pragma unroll
+                for (int i = 0; i < NVMAX; ++i) zv[i] = (int32_t)wv[i] >> 16;
               } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(mp);
-                wv[0] = v.x, wv[1] = v.y;
+                const uint32_t* sp = pw + i16 * ssw + g0 / 2;
+                const int32_t* zp = reinterpret_cast<const int32_t*>(pw + 16 * ssw + i16 * zsw + g0);
+                if constexpr (NVMAX == 4) {
+                  const uint2 v = *reinterpret_cast<const uint2*>(sp);
+                  wv[0] = v.x, wv[1] = v.x >> 16, wv[2] = v.y, wv[3] = v.y >> 16;
+                  const int4 z4 = *reinterpret_cast<const int4*>(zp);
+                  zv[0] = z4.x, zv[1] = z4.y, zv[2] = z4.z, zv[3] = z4.w;
+                } else {
+                  const uint32_t v = *sp;
+                  wv[0] = v, wv[1] = v >> 16;
+                  const int2 z2 = *reinterpret_cast<const int2*>(zp);
+                  zv[0] = z2.x, zv[1] = z2.y;
+                }
               }
 #pragma unroll
-              for (int i = 0; i < NVMAX; ++i) zv[i] = (int32_t)wv[i] >> 16;
+              for (int i = 0; i < NVMAX; ++i) sv[i] = (uint16_t)wv[i];
             } else {
-              const uint32_t* sp = pw + i16 * ssw + g0 / 2;
-              const int32_t* zp = reinterpret_cast<const int32_t*>(pw + 16 * ssw + i16 * zsw + g0);
-              if constexpr (NVMAX == 4) {
-                const uint2 v = *reinterpret_cast<const uint2*>(sp);
-                wv[0] = v.x, wv[1] = v.x >> 16, wv[2] = v.y, wv[3] = v.y >> 16;
-                const int4 z4 = *reinterpret_cast<const int4*>(zp);
-                zv[0] = z4.x, zv[1] = z4.y, zv[2] = z4.z, zv[3] = z4.w;
-              } else {
-                const uint32_t v = *sp;
-                wv[0] = v, wv[1] = v >> 16;
-                const int2 z2 = *reinterpret_cast<const int2*>(zp);
-                zv[0] = z2.x, zv[1] = z2.y;
+              rp.template at_vec<NVMAX>(g0, sv, zv);
+            }
+#pragma unroll
+            for (int u = 0; u < NWMAX; ++u)
+              if (run_start(u) == u) {
+                const int i = kRuns2 ? u >> 1 : u;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                  b.hp[u][c] = HalfParams{sv[i], sv[i], zv[i], zv[i], true, true};
               }
-            }
-#pragma unroll
-            for (int i = 0; i < NVMAX; ++i) sv[i] = (uint16_t)wv[i];
           } else {
-            rp.template at_vec<NVMAX>(g0, sv, zv);
+#pragma unroll
+            for (int u = 0; u < NWMAX; ++u)
+              if (run_start(u) == u) {
+                const UnitRef ur = my_unit(t, u < NW ? u : 0);
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                  b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
+              }
           }
-#pragma unroll
-          for (int u = 0; u < NWMAX; ++u)
-            if (run_start(u) == u) {
-              const int i = kRuns2 ? u >> 1 : u;
-#pragma unroll
-              for (int c = 0; c < NC; ++c)
-                b.hp[u][c] = HalfParams{sv[i], sv[i], zv[i], zv[i], true, true};
-            }
-        } else {
-#pragma unroll
-          for (int u = 0; u < NWMAX; ++u)
-            if (run_start(u) == u) {
-              const UnitRef ur = my_unit(t, u < NW ? u : 0);
-#pragma unroll
-              for (int c = 0; c < NC; ++c)
-                b.hp[u][c] = params_at<BITS, GM, META>(rp, gsz, gshift, ur, c, K);
-            }
         }
       }
     };
@@ -425,6 +480,43 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
       // afterwards (per unit for groups).  Other group layouts: the exact
       // dequantized value (q - z) * s enters as two fp16 operands, its fp16
       // rounding hi and the exact remainder lo, one MFMA each.
+      // Staged step parameters of this lane's row (see kStepStage): group
+      // i of the step belongs to run i.
+      HalfParams shp[NVMAX];
+      if constexpr (kStepStage) {
+        {
+          const uint32_t* d = ps + buf * 1024 + 8 * (16 * gl + i16);
+          uint16_t sv[NVMAX];
+          int32_t zv[NVMAX];
+          uint32_t wv[NVMAX];
+          if constexpr (NVMAX == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(d + 4);
+            wv[0] = v.x, wv[1] = v.y, wv[2] = v.z, wv[3] = v.w;
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(d + 4);
+            wv[0] = v.x, wv[1] = v.y;
+          }
+          if constexpr (META) {
+#pragma unroll
+            for (int i = 0; i < NVMAX; ++i) sv[i] = (uint16_t)wv[i], zv[i] = (int32_t)wv[i] >> 16;
+          } else {
+            uint32_t s2[2];
+            if constexpr (NVMAX == 4) {
+              const uint2 v = *reinterpret_cast<const uint2*>(d);
+              s2[0] = v.x, s2[1] = v.y;
+            } else {
+              s2[0] = d[0], s2[1] = 0u;
+            }
+#pragma unroll
+            for (int i = 0; i < NVMAX; ++i) {
+              sv[i] = (uint16_t)(s2[i >> 1] >> (16 * (i & 1)));
+              zv[i] = (int32_t)wv[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < NVMAX; ++i) shp[i] = HalfParams{sv[i], sv[i], zv[i], zv[i], true, true};
+        }
+      }
 #pragma unroll
       for (int u = 0; u < NWMAX; ++u) {
         if (u < NW) {
@@ -439,7 +531,10 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
               cc[c] = rowc;
               fast = rowfast;
             } else {
-              hp[c] = b.hp[GM == kWideGroups ? run_start(u) : u][c];
+              if constexpr (kStepStage)
+                hp[c] = shp[kRuns2 ? u >> 1 : u];
+              else
+                hp[c] = b.hp[GM == kWideGroups ? run_start(u) : u][c];
               fast &= make_pconsts<BITS>(hp[c], cc[c], DIRECT);
             }
             hp[c].v_lo = ur.va;
@@ -538,19 +633,29 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     WBuf wa, wb;
     fetch_x(0);
     load_w(0, wa);
+    if constexpr (kStepStage) fetch_p(0);
     store_x(0);
+    if constexpr (kStepStage) store_p(0);
     __syncthreads();
     for (int t = 0; t < T; t += 2) {
       fetch_x(min(t + 1, T - 1));
       load_w(min(t + 1, T - 1), wb);
+      if constexpr (kStepStage) fetch_p(min(t + 1, T - 1));
       compute(t, 0, wa);
-      if (t + 1 < T) store_x(1);
+      if (t + 1 < T) {
+        store_x(1);
+        if constexpr (kStepStage) store_p(1);
+      }
       __syncthreads();
       if (t + 1 >= T) break;
       fetch_x(min(t + 2, T - 1));
       load_w(min(t + 2, T - 1), wa);
+      if constexpr (kStepStage) fetch_p(min(t + 2, T - 1));
       compute(t + 1, 1, wb);
-      if (t + 2 < T) store_x(0);
+      if (t + 2 < T) {
+        store_x(0);
+        if constexpr (kStepStage) store_p(0);
+      }
       __syncthreads();
     }
 
@@ -580,7 +685,19 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
   }
 }
 
-template <int BITS, int BT, int GM, bool META>
+// Every round of every workgroup takes at least five 16-row groups (one K
+// part per round): workgroups own ng or ng + 1 groups, walked in rounds of
+// eight.
+inline bool rounds_one_part(int N) {
+  const int NG = (N + 15) / 16;
+  const int cus = device_cu_count();
+  const int nwg = NG < cus ? NG : cus;
+  const int gb = NG / nwg, ge = NG % nwg;
+  auto ok = [](int ng) { return ng >= 5 && (ng % kWaves == 0 || ng % kWaves >= 5); };
+  return (nwg == ge || ok(gb)) && (ge == 0 || ok(gb + 1));
+}
+
+template <int BITS, int BT, int GM, bool META, bool SS = false>
 hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint16_t* scales,
                     const int32_t* zeros, int N, int K, int G, int gsz, int gshift, uint16_t* y,
                     hipStream_t stream) {
@@ -590,6 +707,24 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
   // wave's scales and zeros in LDS when they fit (the kernel's layout:
   // strides G/2 + 2 and G + 4 words per row, 16 rows per wave)
   int pstage = 0;
+  if constexpr (GM == kWideGroups && BT == 4 && BITS != 8) {
+    // 64-row batch tiles: the variant that stages each step's parameters
+    // (8 KB, see the kernel) when the group is exactly one run's span, K is
+    // whole steps, the arrays are 16-byte aligned and every round has one K
+    // part (not at 8 bits, where its registers would spill more)
+    const size_t extra = 2 * 1024 * 4;
+    if constexpr (SS) {
+      lds += extra;
+    } else {
+      const int span = 4 * (BITS == 8 ? 2 : 1) * Unit<BITS>::CODES;
+      const bool aligned = reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
+                           (META || reinterpret_cast<uintptr_t>(zeros) % 16 == 0);
+      if (gsz == span && K % kTileK == 0 && aligned && rounds_one_part(N) &&
+          lds + extra <= device_lds_per_block())
+        return launch_t<BITS, BT, GM, META, true>(x, B, packed, scales, zeros, N, K, G, gsz,
+                                                  gshift, y, stream);
+    }
+  }
   if (GM == kWideGroups && BT <= 2) {
     const int span = 4 * (BITS == 8 ? 2 : 1) * Unit<BITS>::CODES;
     const size_t pww = META ? 16 * (size_t)(G + 4) : 16 * (size_t)(G / 2 + 2 + G + 4);
@@ -601,7 +736,7 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
       lds += extra;
     }
   }
-  const auto kern = qgemm_kernel<BITS, BT, GM, META>;
+  const auto kern = qgemm_kernel<BITS, BT, GM, META, SS>;
   // the LDS request exceeds the default limit: raise it, once per device, to
   // the most any launch of this kernel can ask for
   const hipError_t e =
