@@ -707,11 +707,11 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
   // wave's scales and zeros in LDS when they fit (the kernel's layout:
   // strides G/2 + 2 and G + 4 words per row, 16 rows per wave)
   int pstage = 0;
-  if constexpr (GM == kWideGroups && BT == 4 && BITS != 8) {
+  if constexpr (GM == kWideGroups && BT == 4) {
     // 64-row batch tiles: the variant that stages each step's parameters
     // (8 KB, see the kernel) when the group is exactly one run's span, K is
     // whole steps, the arrays are 16-byte aligned and every round has one K
-    // part (not at 8 bits, where its registers would spill more)
+    // part
     const size_t extra = 2 * 1024 * 4;
     if constexpr (SS) {
       lds += extra;
