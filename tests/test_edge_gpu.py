@@ -330,6 +330,38 @@ def test_qgemm_staged_group_parameters(lw, bits, N, K, g):
     harness.assert_y_close(y48.cpu().numpy(), y_ref, f"qgemm bits={bits} N={N} K={K} g={g} B=48")
 
 
+# 64-row batch tiles stage each step's group parameters in LDS when every
+# round of every workgroup (one per CU, 256 CUs) holds at least five 16-row
+# groups: 13 groups per workgroup (rounds of 8 and 5: staged), 12 (8 and 4:
+# loaded per lane), and shares of 5 and 6 groups with a ragged last tile
+# (staged).  Each must match the oracle, give the same bits from compact group
+# words, and give the 16-row tile's bits in its first 16 rows (the same K
+# split, parameters copied per round or loaded per step).
+STEP_STAGED_CASES = [(4, 13 * 256 * 16, 1024, 128), (4, 12 * 256 * 16, 1024, 128),
+                     (4, (5 * 256 + 100) * 16 - 3, 1024, 128), (2, 13 * 256 * 16, 1024, 256),
+                     (8, (5 * 256 + 100) * 16 - 3, 1024, 128)]
+
+
+@pytest.mark.parametrize("bits,N,K,g", STEP_STAGED_CASES)
+def test_qgemm_step_staged_parameters(lw, bits, N, K, g):
+    import torch
+    _say(f"[step-staged parameters] bits={bits} N={N} K={K} g={g}")
+    w = _weights("mixed", N, K, seed=N + 31 * K + bits)
+    codes, scales, zeros, packed = harness.oracle_quantize(w, bits, g)
+    p, s, z = _to_gpu(packed), _to_gpu(scales), _to_gpu(zeros)
+    meta = lw.pack_meta(s, z)
+    x = harness.synth.normal_f16(64, K, 1.0, seed=23, stream=2)
+    xg = _to_gpu(x)
+    y64 = lw.qgemm(xg, p, s, z, K, bits, g)
+    m64 = lw.qgemm_meta(xg, p, meta, K, bits, g)
+    y16 = lw.qgemm(xg[:16].contiguous(), p, s, z, K, bits, g)
+    torch.cuda.synchronize()
+    assert torch.equal(m64.view(torch.int16), y64.view(torch.int16)), "compact words"
+    assert torch.equal(y16.view(torch.int16), y64[:16].view(torch.int16)), "B=16 vs B=64"
+    y_ref = harness.oracle_y(x, packed, scales, zeros, K, bits, g)
+    harness.assert_y_close(y64.cpu().numpy(), y_ref, f"qgemm bits={bits} N={N} K={K} g={g} B=64")
+
+
 @pytest.mark.parametrize("kind", ["wide", "tiny", "offset", "mixed", "positive", "negative", "ties"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_products_degenerate(lw, kind, bits):
