@@ -257,9 +257,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_kernel(
     // every wave of the round walks the same step (one K part): stage its
     // parameters cooperatively (see kStepStage)
     constexpr bool sstage = kStepStage;  // (one K part: the host's condition)
-    // Step t's parameters: waves 0-1 load the scales (compact words) of rows
-    // 64 w .. 64 w + 63 of the round, waves 2-3 the zeros, one 16-byte load
-    // per lane; every other wave, and every wave when staging is off, loads
+    // Step t's parameters: waves 0-1 load the scales (compact words) of the
+    // round's rows 64 (w % 2) .. 64 (w % 2) + 63, waves 2-3 the zeros, one
+    // 16-byte load per lane (the groups of the step); every other wave loads
     // from an empty descriptor (zeros, no memory traffic), so each wave
     // issues the same loads on every path.
     const int prole = META ? (wave < 2 ? 0 : 2) : (wave < 4 ? wave >> 1 : 2);  // 0 s, 1 z, 2 none
@@ -719,8 +719,9 @@ hipError_t launch_t(const uint16_t* x, int B, const uint32_t* packed, const uint
       const int span = 4 * (BITS == 8 ? 2 : 1) * Unit<BITS>::CODES;
       const bool aligned = reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
                            (META || reinterpret_cast<uintptr_t>(zeros) % 16 == 0);
+      // (byte offsets into the parameter arrays are 32-bit)
       if (gsz == span && K % kTileK == 0 && aligned && rounds_one_part(N) &&
-          lds + extra <= device_lds_per_block())
+          (int64_t)N * G * 4 <= 0x7fffffff && lds + extra <= device_lds_per_block())
         return launch_t<BITS, BT, GM, META, true>(x, B, packed, scales, zeros, N, K, G, gsz,
                                                   gshift, y, stream);
     }
